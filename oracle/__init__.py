@@ -1,0 +1,227 @@
+"""CPU oracle for the FP4 routed-expert MoE layer (ctypes wrapper of oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``, never by the GPU library or its
+Python binding.  Every function here is the plain definition of one step of
+the layer, computed in fp64 (see the header of ``oracle.c`` for the passages
+of the pages each step follows).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+
+
+def build() -> str:
+    src = os.path.join(_HERE, "oracle.c")
+    tmp = _SO + ".tmp"
+    # -ffp-contract=off: no fused multiply-adds, every product is rounded as written
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                           "-ffp-contract=off", src, "-o", tmp, "-lm"])
+    os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        p, i32, i64, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_uint
+        d = ctypes.c_double
+        lib.orc_e2m1.restype = d
+        lib.orc_e2m1.argtypes = [u]
+        lib.orc_e8m0.restype = d
+        lib.orc_e8m0.argtypes = [u]
+        lib.orc_e4m3.restype = d
+        lib.orc_e4m3.argtypes = [u]
+        lib.orc_bf16.restype = d
+        lib.orc_bf16.argtypes = [ctypes.c_uint16]
+        lib.orc_e4m3_rne_sat.restype = u
+        lib.orc_e4m3_rne_sat.argtypes = [d]
+        lib.orc_decode_fp4_matrix.argtypes = [p, p, i64, i32, p]
+        lib.orc_decode_mxfp8.argtypes = [p, p, i64, i32, p]
+        lib.orc_quant_block32.argtypes = [p, p, p]
+        lib.orc_quant_mxfp8_bf16.argtypes = [p, i64, i32, p, p]
+        lib.orc_quant_mxfp8_f32.argtypes = [p, i64, i32, p, p]
+        lib.orc_route_token.argtypes = [p, i32, i32, p, p]
+        lib.orc_route.argtypes = [p, i64, i32, i32, p, p]
+        lib.orc_sort.argtypes = [p, i64, i32, p, p, p, p]
+        lib.orc_expert_gate_up.argtypes = [p, p, i32, i32, p, p, p, p, p, p]
+        lib.orc_swiglu_requant.argtypes = [p, p, i32, p, p, p]
+        lib.orc_expert_down.argtypes = [p, p, i32, i32, p, p, p]
+        lib.orc_layer_tokens.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p, p, p,
+                                         p, i64, p, p, p, p]
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "contiguous numpy array required"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ decoders
+def e2m1(code: int) -> float:
+    return _load().orc_e2m1(code)
+
+
+def e8m0(code: int) -> float:
+    return _load().orc_e8m0(code)
+
+
+def e4m3(byte: int) -> float:
+    return _load().orc_e4m3(byte)
+
+
+def bf16(bits: int) -> float:
+    return _load().orc_bf16(bits)
+
+
+def e4m3_rne_sat(a: float) -> int:
+    return int(_load().orc_e4m3_rne_sat(float(a)))
+
+
+def decode_fp4_matrix(w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Packed e2m1 [rows, K/2] + scales [rows, K/32] -> float64 [rows, K]."""
+    w = _c(w, np.uint8)
+    s = _c(s, np.uint8)
+    K = w.shape[-1] * 2
+    rows = w.size // w.shape[-1]
+    out = np.empty(w.shape[:-1] + (K,), dtype=np.float64)
+    _load().orc_decode_fp4_matrix(_p(w), _p(s), rows, K, _p(out))
+    return out
+
+
+def decode_mxfp8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    K = q.shape[-1]
+    rows = q.size // K
+    out = np.empty(q.shape, dtype=np.float64)
+    _load().orc_decode_mxfp8(_p(q), _p(s), rows, K, _p(out))
+    return out
+
+
+# -------------------------------------------------------------- quantisation
+def quant_block32(v) -> tuple[np.ndarray, int]:
+    v = _c(v, np.float64)
+    assert v.shape == (32,)
+    q = np.empty(32, dtype=np.uint8)
+    s = np.empty(1, dtype=np.uint8)
+    _load().orc_quant_block32(_p(v), _p(q), _p(s))
+    return q, int(s[0])
+
+
+def quant_mxfp8_bf16(x_bits: np.ndarray):
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // 32), dtype=np.uint8)
+    _load().orc_quant_mxfp8_bf16(_p(x), M, K, _p(q), _p(s))
+    return q, s
+
+
+def quant_mxfp8_f32(x: np.ndarray):
+    x = _c(x, np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // 32), dtype=np.uint8)
+    _load().orc_quant_mxfp8_f32(_p(x), M, K, _p(q), _p(s))
+    return q, s
+
+
+# -------------------------------------------------------------- route / sort
+def route(logits: np.ndarray, k: int):
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    gates = np.empty((T, k), dtype=np.float32)
+    _load().orc_route(_p(lg), T, E, k, _p(ids), _p(gates))
+    return ids, gates
+
+
+def sort(ids: np.ndarray, E: int):
+    ids = _c(ids, np.int32).reshape(-1)
+    P = ids.size
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    sorted_pair = np.empty(P, dtype=np.int32)
+    pair_pos = np.empty(P, dtype=np.int32)
+    _load().orc_sort(_p(ids), P, E, _p(counts), _p(offsets), _p(sorted_pair), _p(pair_pos))
+    return counts, offsets, sorted_pair, pair_pos
+
+
+# ------------------------------------------------------------------- experts
+def expert_gate_up(xq_row, xs_row, w1e, s1e, w3e, s3e):
+    xq_row = _c(xq_row, np.uint8)
+    xs_row = _c(xs_row, np.uint8)
+    I, Hh = w1e.shape
+    H = Hh * 2
+    G = np.empty(I, dtype=np.float64)
+    U = np.empty(I, dtype=np.float64)
+    _load().orc_expert_gate_up(_p(xq_row), _p(xs_row), H, I, _p(_c(w1e, np.uint8)),
+                               _p(_c(s1e, np.uint8)), _p(_c(w3e, np.uint8)),
+                               _p(_c(s3e, np.uint8)), _p(G), _p(U))
+    return G, U
+
+
+def swiglu_requant(G, U):
+    G = _c(G, np.float64)
+    U = _c(U, np.float64)
+    I = G.size
+    h = np.empty(I, dtype=np.float32)
+    hq = np.empty(I, dtype=np.uint8)
+    hs = np.empty(I // 32, dtype=np.uint8)
+    _load().orc_swiglu_requant(_p(G), _p(U), I, _p(h), _p(hq), _p(hs))
+    return h, hq, hs
+
+
+def expert_down(hq, hs, w2e, s2e):
+    hq = _c(hq, np.uint8)
+    hs = _c(hs, np.uint8)
+    H, Ih = w2e.shape
+    I = Ih * 2
+    O = np.empty(H, dtype=np.float64)
+    _load().orc_expert_down(_p(hq), _p(hs), H, I, _p(_c(w2e, np.uint8)), _p(_c(s2e, np.uint8)), _p(O))
+    return O
+
+
+def layer_tokens(inp, tokens=None, want_pairs: bool = False):
+    """The layer's output rows y[t] (float32 [len(tokens), H]) for the given tokens.
+
+    ``inp`` is a ``synth.LayerInputs``.  With ``want_pairs`` also returns the
+    per-(token, slot) h (fp32), hq and hs.
+    """
+    sh = inp.shape
+    T, H, I, E, k = sh.T, sh.H, sh.I, sh.E, sh.k
+    toks = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
+    n = toks.size
+    y = np.empty((n, H), dtype=np.float32)
+    h = hq = hs = None
+    if want_pairs:
+        h = np.empty((n * k, I), dtype=np.float32)
+        hq = np.empty((n * k, I), dtype=np.uint8)
+        hs = np.empty((n * k, I // 32), dtype=np.uint8)
+    _load().orc_layer_tokens(_p(_c(inp.x, np.uint16)), _p(_c(inp.logits, np.float32)), H, I, E, k,
+                             _p(inp.w1), _p(inp.s1), _p(inp.w3), _p(inp.s3), _p(inp.w2), _p(inp.s2),
+                             _p(toks), n, _p(y), _p(h), _p(hq), _p(hs))
+    if want_pairs:
+        return y, h, hq, hs
+    return y
