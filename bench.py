@@ -1,0 +1,177 @@
+"""Benchmark of the FP4 routed-expert MoE layer on one MI355X.
+
+One step = the whole layer on one batch of synthetic inputs already resident
+in HBM: moe_route_topk -> moe_sort_permute -> moe_quant_act_mxfp8 ->
+moe_fp4_expert_up -> moe_fp4_expert_down -> moe_combine, all on one stream.
+The default workload is the decode-shaped layer (T=8, H=4096, I=1536, E=64,
+top-6).  Several copies of the packed weights are cycled so that the 256 MB
+Infinity Cache cannot serve a step's weights from the previous step.
+
+Prints ONE JSON line (rank 0).  The dominant kernel (the gate/up expert GEMM)
+is timed with HIP events on the stream it runs on, and its algorithmic bytes
+per launch give the roofline fraction against 8 TB/s.  The CPU baseline is the
+oracle (a plain fp64 C implementation) on the host's cores, on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 (and FP8 x FP4 scaled MFMA at the FP8 issue rate)
+METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU"
+
+
+def weight_bytes_per_expert(H: int, I: int, mats: int) -> float:
+    # packed e2m1 nibbles (1/2 B) + one E8M0 byte per 32 elements
+    return mats * H * I * (0.5 + 1.0 / 32)
+
+
+def cpu_baseline(name: str, budget_s: float):
+    import oracle
+    import synth
+    inp = synth.make_inputs(name)
+    T = inp.shape.T
+    oracle.layer_tokens(inp, np.arange(1, dtype=np.int32))  # warm the page cache
+    n_tok = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.layer_tokens(inp)
+        n_tok += T
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole layer, all {T} tokens of the {name} workload, repeated "
+                      f"{n_tok // T}x in {dt:.1f} s (fp64 plain C, OpenMP)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1", help="workload name (c1 is the measured one)")
+    ap.add_argument("--flags", type=int, default=0, help="1 = force decode path, 2 = force prefill path")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 = skip")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0 = auto)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp4_routed_expert_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(args.config)
+    sh = inp.shape
+    T, H, I, E, k = sh.T, sh.H, sh.I, sh.E, sh.k
+    P = T * k
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    canon = [t(getattr(inp, n)) for n in ("w1", "s1", "w3", "s3", "w2", "s2")]
+    packed_bytes = moe.packed_weight_bytes(E, H, I)
+    copies = args.copies or max(1, min(8, int(np.ceil(2.0e9 / packed_bytes))))
+    pws = [moe.prepack_weights(*canon) for _ in range(copies)]
+    del canon
+    x = t(inp.x.view(np.int16)).view(torch.bfloat16)
+    logits = t(inp.logits)
+
+    # all outputs and workspaces allocated once, outside the timed region
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sort_out = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+                torch.empty(P, dtype=torch.int32, device=dev), torch.empty(P, dtype=torch.int32, device=dev))
+    from fp4_routed_expert_amd import _lib
+    sort_ws_n = _lib.lib().moe_sort_permute_workspace_size(T, E, k)
+    sort_ws = torch.empty(max(sort_ws_n, 256), dtype=torch.uint8, device=dev)
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    hq = torch.empty((P, I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((P, I // 32), dtype=torch.uint8, device=dev)
+    O = torch.empty((P, H), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, k, E), 256),
+                           dtype=torch.uint8, device=dev)
+    nsteps = args.warmup + args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i, timed_idx=None):
+        pw = pws[i % copies]
+        moe.route_topk(logits, k, ids, gates)
+        counts, offsets, sp, pp = moe.sort_permute(ids, E, out=sort_out, workspace=sort_ws)
+        moe.quant_act_mxfp8(x, xq, xs)
+        if timed_idx is not None:
+            ev[timed_idx][0].record()
+        moe.expert_up(pw, xq, xs, offsets, sp, T, k, args.flags, hq=hq, hs=hs, workspace=stage_ws)
+        if timed_idx is not None:
+            ev[timed_idx][1].record()
+        moe.expert_down(pw, hq, hs, offsets, T, k, args.flags, O=O, workspace=stage_ws)
+        moe.combine(O, gates, pp, T, k, H, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    counts = sort_out[0].cpu().numpy()
+    used = int((counts > 0).sum())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dt = t1 - t0
+    up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_per_step = dt / args.steps * 1e3
+    tokens_per_s = T * args.steps / dt
+    # algorithmic bytes: weights of the experts that tokens were routed to, plus activations
+    b_layer = used * weight_bytes_per_expert(H, I, 3) + T * H * 2 + T * E * 4 + T * H * 4
+    b_up = used * weight_bytes_per_expert(H, I, 2) + T * H * (1 + 1 / 32) + P * I * (1 + 1 / 32)
+    up_gbs = b_up / (up_ms * 1e-3) / 1e9
+    flops = 6.0 * H * I * P
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4e2m1xfp8e4m3->fp32",
+        "data": "synthetic",
+        "config": {"workload": synth.CONFIG_NAMES.get(args.config, args.config), "T": T, "H": H, "I": I,
+                   "E": E, "k": k, "seed": sh.seed, "used_experts": used, "weight_copies": copies,
+                   "path_flags": args.flags},
+        "layer_hbm_tbps": b_layer / (ms_per_step * 1e-3) / 1e12,
+        "layer_hbm_frac": b_layer / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "layer_mfma_frac_fp8": flops / (ms_per_step * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "kernel": "up_decode_kernel (gate/up GEMM + SwiGLU + MXFP8)",
+                     "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": up_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": b_up, "avg_launch_us": up_ms * 1e3},
+    }
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

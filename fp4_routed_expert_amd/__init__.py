@@ -1,0 +1,213 @@
+"""MI355X-native FP4 routed-expert MoE layer: thin Python binding.
+
+Every function marshals torch tensors (device memory) and the current HIP
+stream into one call of the C ABI in ``include/moe_fp4.h``; every step of the
+layer runs in the gfx950 kernels of ``libmoe_fp4.so``.  PyTorch provides
+device memory and streams only.
+
+    pw = prepack_weights(w1, s1, w3, s3, w2, s2)          # once, at load time
+    y  = moe_layer(pw, x_bf16, logits, k)                  # route/sort/quant/experts/combine
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_FLAG_FORCE_DECODE, MOE_FLAG_FORCE_PREFILL, MoeError,  # noqa: F401
+                   MoeFp4Weights)
+
+__all__ = [
+    "route_topk", "sort_permute", "quant_act_mxfp8", "prepack_weights", "PackedWeights",
+    "expert_up", "expert_down", "combine", "grouped_forward", "moe_layer",
+    "forward_workspace_size", "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
+]
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda:
+        raise ValueError("device tensor required")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor required")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dtype(t: torch.Tensor, dtypes, name: str):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+def route_topk(logits: torch.Tensor, k: int, ids: torch.Tensor | None = None,
+               gates: torch.Tensor | None = None):
+    """logits [T, E] fp32 -> (topk_ids [T, k] int32, topk_gates [T, k] fp32)."""
+    _check_dtype(logits, (torch.float32,), "logits")
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if gates is None:
+        gates = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _lib.check(_lib.lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(gates),
+                                         _stream(logits)), "moe_route_topk")
+    return ids, gates
+
+
+def sort_permute(ids: torch.Tensor, E: int, out=None, workspace: torch.Tensor | None = None):
+    """topk_ids [T, k] -> (counts [E], offsets [E+1], sorted_pair [T*k], pair_pos [T*k])."""
+    _check_dtype(ids, (torch.int32,), "topk_ids")
+    T, k = ids.shape
+    dev = ids.device
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev))
+    counts, offsets, sp, pp = out
+    L = _lib.lib()
+    need = L.moe_sort_permute_workspace_size(T, E, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel()
+    _lib.check(L.moe_sort_permute(_ptr(ids), T, E, k, _ptr(counts), _ptr(offsets), _ptr(sp),
+                                  _ptr(pp), _ptr(workspace), wsb, _stream(ids)),
+               "moe_sort_permute")
+    return counts, offsets, sp, pp
+
+
+def quant_act_mxfp8(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+    """x [M, K] bf16 -> (q [M, K] e4m3fn bytes as uint8, s [M, K/32] E8M0 codes as uint8)."""
+    _check_dtype(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _lib.check(_lib.lib().moe_quant_act_mxfp8(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)),
+               "moe_quant_act_mxfp8")
+    return q, s
+
+
+@dataclasses.dataclass
+class PackedWeights:
+    """Prepacked expert weights: the device buffer plus the plain-C descriptor."""
+    buffer: torch.Tensor
+    desc: MoeFp4Weights
+
+    @property
+    def E(self):
+        return self.desc.E
+
+    @property
+    def H(self):
+        return self.desc.H
+
+    @property
+    def I(self):
+        return self.desc.I
+
+
+def packed_weight_bytes(E: int, H: int, I: int) -> int:
+    return int(_lib.lib().moe_fp4_packed_weight_bytes(E, H, I))
+
+
+def prepack_weights(w1, s1, w3, s3, w2, s2) -> PackedWeights:
+    """Canonical packed-e2m1 weights + E8M0 scales (uint8 device tensors):
+    w1, w3 [E, I, H/2], s1, s3 [E, I, H/32], w2 [E, H, I/2], s2 [E, H, I/32]."""
+    for name, t in (("w1", w1), ("s1", s1), ("w3", w3), ("s3", s3), ("w2", w2), ("s2", s2)):
+        _check_dtype(t, (torch.uint8,), name)
+    E, I, Hh = w1.shape
+    H = Hh * 2
+    nbytes = packed_weight_bytes(E, H, I)
+    if nbytes == 0:
+        raise MoeError(_lib.MOE_ERR_UNSUPPORTED, "moe_fp4_packed_weight_bytes")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=w1.device)
+    desc = MoeFp4Weights()
+    _lib.check(_lib.lib().moe_fp4_prepack_weights(
+        _ptr(w1), _ptr(s1), _ptr(w3), _ptr(s3), _ptr(w2), _ptr(s2), E, H, I, _ptr(buf), nbytes,
+        ctypes.byref(desc), _stream(w1)), "moe_fp4_prepack_weights")
+    return PackedWeights(buffer=buf, desc=desc)
+
+
+def _stage_ws(T, k, E, dev, workspace):
+    need = _lib.lib().moe_fp4_stage_workspace_size(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def expert_up(pw: PackedWeights, xq, xs, offsets, sorted_pair, T: int, k: int, flags: int = 0,
+              hq=None, hs=None, workspace=None):
+    """Gate/up GEMM + SwiGLU + MXFP8 of h -> (hq [T*k, I], hs [T*k, I/32]), sorted order."""
+    dev = xq.device
+    P = T * k
+    if hq is None:
+        hq = torch.empty((P, pw.I), dtype=torch.uint8, device=dev)
+    if hs is None:
+        hs = torch.empty((P, pw.I // 32), dtype=torch.uint8, device=dev)
+    workspace = _stage_ws(T, k, pw.E, dev, workspace)
+    _lib.check(_lib.lib().moe_fp4_expert_up(
+        ctypes.byref(pw.desc), _ptr(xq), _ptr(xs), _ptr(offsets), _ptr(sorted_pair), T, k, _ptr(hq),
+        _ptr(hs), _ptr(workspace), workspace.numel(), flags, _stream(xq)), "moe_fp4_expert_up")
+    return hq, hs
+
+
+def expert_down(pw: PackedWeights, hq, hs, offsets, T: int, k: int, flags: int = 0, O=None,
+                workspace=None):
+    """Down GEMM -> O [T*k, H] fp32, sorted order."""
+    dev = hq.device
+    if O is None:
+        O = torch.empty((T * k, pw.H), dtype=torch.float32, device=dev)
+    workspace = _stage_ws(T, k, pw.E, dev, workspace)
+    _lib.check(_lib.lib().moe_fp4_expert_down(
+        ctypes.byref(pw.desc), _ptr(hq), _ptr(hs), _ptr(offsets), T, k, _ptr(O), _ptr(workspace),
+        workspace.numel(), flags, _stream(hq)), "moe_fp4_expert_down")
+    return O
+
+
+def combine(O, gates, pair_pos, T: int, k: int, H: int, y=None):
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=O.device)
+    _lib.check(_lib.lib().moe_combine(_ptr(O), _ptr(gates), _ptr(pair_pos), T, k, H, _ptr(y),
+                                      _stream(O)), "moe_combine")
+    return y
+
+
+def forward_workspace_size(T: int, k: int, E: int, H: int, I: int, flags: int = 0) -> int:
+    return int(_lib.lib().moe_fp4_forward_workspace_size(T, k, E, H, I, flags))
+
+
+def grouped_forward(pw: PackedWeights, xq, xs, gates, offsets, sorted_pair, pair_pos, flags: int = 0,
+                    y=None, workspace=None):
+    """Expert GEMMs + combine -> y [T, H] fp32."""
+    T, k = gates.shape
+    dev = xq.device
+    if y is None:
+        y = torch.empty((T, pw.H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = forward_workspace_size(T, k, pw.E, pw.H, pw.I, flags)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _lib.check(_lib.lib().moe_fp4_grouped_forward(
+        ctypes.byref(pw.desc), _ptr(xq), _ptr(xs), _ptr(gates), _ptr(offsets), _ptr(sorted_pair),
+        _ptr(pair_pos), T, k, _ptr(y), _ptr(workspace), workspace.numel(), flags, _stream(xq)),
+        "moe_fp4_grouped_forward")
+    return y
+
+
+def moe_layer(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: int, flags: int = 0,
+              return_intermediates: bool = False):
+    """The whole layer: route -> sort/permute -> MXFP8(x) -> experts -> combine."""
+    ids, gates = route_topk(logits, k)
+    counts, offsets, sp, pp = sort_permute(ids, pw.E)
+    xq, xs = quant_act_mxfp8(x)
+    y = grouped_forward(pw, xq, xs, gates, offsets, sp, pp, flags)
+    if return_intermediates:
+        return y, dict(topk_ids=ids, topk_gates=gates, expert_counts=counts, expert_offsets=offsets,
+                       sorted_pair=sp, pair_pos=pp, xq=xq, xs=xs)
+    return y

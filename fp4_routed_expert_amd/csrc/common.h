@@ -1,0 +1,174 @@
+// Internal header of the gfx950 MoE library: device helpers, the packed
+// weight layout, and the launchers each kernel file provides to moe_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- MXFP8
+// OCP MX conversion of one 32-element block: shared exponent
+// X = floor(log2 amax) - 8, X = -127 when amax is zero or below the fp32
+// normal range, scale code X + 127.  Returned: the scale code; *mul is the
+// exact power of two 2^-X to multiply each element by before rounding.
+__device__ __forceinline__ uint32_t mx_scale_from_amax(float amax, float* mul) {
+  const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFFu;  // amax >= 0
+  int X = (ef == 0u) ? -127 : (int)ef - 135;
+  if (X < -127) X = -127;  // ef <= 254 keeps X <= 119
+  *mul = __uint_as_float((uint32_t)(127 - X) << 23);
+  return (uint32_t)(X + 127);
+}
+
+// Round an fp32 value (|a| < 512 after scaling) to an OCP e4m3fn code:
+// nearest, ties to even, saturating at 448, sign kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag >= 0x43E00000u) return sign | 0x7Eu;             // >= 448
+  if (mag < 0x3C800000u) {                                  // < 2^-6: steps of 2^-9
+    const float m = __uint_as_float(mag) * 512.0f;          // exact
+    return sign | (uint32_t)__builtin_rintf(m);             // 0..8 (8 = 2^-6)
+  }
+  // keep 3 of the 23 mantissa bits, round to nearest even on the bit pattern;
+  // a carry moves into the exponent field, which is the correct next binade
+  const uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);
+  return sign | ((r >> 20) - (120u << 3));                  // rebias 127 -> 7
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// ------------------------------------------------------------------ scans
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan of a[0..n) in LDS (n <= 1024) by a 256-thread block; returns
+// the total.  Each thread owns 4 consecutive entries; wave_tot is LDS [4].
+__device__ __forceinline__ int block_exclusive_scan256(int* a, int n, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * tid + i;
+    v[i] = idx < n ? a[idx] : 0;
+    s += v[i];
+  }
+  const int incl = wave_inclusive_scan(s, lane);
+  if (lane == 63) wave_tot[w] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    before += (i < w) ? wave_tot[i] : 0;
+    total += wave_tot[i];
+  }
+  int run = before + incl - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * tid + i;
+    if (idx < n) a[idx] = run;
+    run += v[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// ------------------------------------------------------ packed weight layout
+// Every weight tile is the B operand of one v_mfma_scale_f32_16x16x128_f8f6f4:
+// 16 output rows x 128 K, 1 KiB, stored in lane order: lane l holds row
+// (l & 15) and K elements [32*(l >> 4), +32) as 16 consecutive bytes (even K
+// in the low nibble), i.e. exactly one 32-element scale block per lane.
+//
+// Region UPW (gate/up weights): per expert e, per 32-row group q of I, per
+// K-step j of H/128: 4 tiles of 1 KiB = [W1 rows 32q..+16, W1 rows 32q+16..+16,
+//                                        W3 rows 32q..+16, W3 rows 32q+16..+16]
+// Region UPS (their scales): per (e, q, jg = j/4): 4 tiles x 64 lanes x 4 B;
+//   byte b of a lane's dword is that lane's scale in K-step 4*jg + b.
+// Region DNW (down weights): per expert e, per 32-row group q2 of H, per
+//   K-step j2 of I/128: 2 tiles = [W2 rows 32q2..+16, 32q2+16..+16].
+// Region DNS (their scales): per (e, q2, jg2): 2 tiles x 64 lanes x 4 B.
+struct PackedLayout {
+  int E, H, I;
+  int J, JG;    // gate/up K-steps (H/128) and scale groups ceil(J/4)
+  int J2, JG2;  // down K-steps (I/128) and scale groups
+  size_t upw_off, ups_off, dnw_off, dns_off, total;
+
+  __host__ __device__ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+  __host__ __device__ PackedLayout(int E_, int H_, int I_) : E(E_), H(H_), I(I_) {
+    J = H / 128;
+    JG = (J + 3) / 4;
+    J2 = I / 128;
+    JG2 = (J2 + 3) / 4;
+    const size_t upw = (size_t)E * (I / 32) * J * 4096;
+    const size_t ups = (size_t)E * (I / 32) * JG * 1024;
+    const size_t dnw = (size_t)E * (H / 32) * J2 * 2048;
+    const size_t dns = (size_t)E * (H / 32) * JG2 * 512;
+    upw_off = 0;
+    ups_off = align256(upw_off + upw);
+    dnw_off = align256(ups_off + ups);
+    dns_off = align256(dnw_off + dnw);
+    total = align256(dns_off + dns);
+  }
+  // byte offset of the 4 KiB gate/up block (e, q, j)
+  __host__ __device__ size_t upw_block(int e, int q, int j) const {
+    return upw_off + (((size_t)e * (I / 32) + q) * J + j) * 4096;
+  }
+  __host__ __device__ size_t ups_block(int e, int q, int jg) const {
+    return ups_off + (((size_t)e * (I / 32) + q) * JG + jg) * 1024;
+  }
+  __host__ __device__ size_t dnw_block(int e, int q2, int j2) const {
+    return dnw_off + (((size_t)e * (H / 32) + q2) * J2 + j2) * 2048;
+  }
+  __host__ __device__ size_t dns_block(int e, int q2, int jg2) const {
+    return dns_off + (((size_t)e * (H / 32) + q2) * JG2 + jg2) * 512;
+  }
+};
+
+// ------------------------------------------------------------- launchers
+// Each returns the hipError_t of its launch(es).
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids,
+                             float* gates, hipStream_t s);
+size_t sort_workspace_bytes(int T, int E, int k);
+hipError_t launch_sort_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                               void* ws, hipStream_t s);
+hipError_t launch_quant_mxfp8(const uint16_t* x, long M, int K, uint8_t* q, uint8_t* sc,
+                              hipStream_t s);
+hipError_t launch_prepack(const uint8_t* w1, const uint8_t* s1, const uint8_t* w3,
+                          const uint8_t* s3, const uint8_t* w2, const uint8_t* s2,
+                          const PackedLayout& L, uint8_t* packed, hipStream_t s);
+hipError_t launch_up_decode(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
+                            const uint8_t* xs, const int32_t* offsets,
+                            const int32_t* sorted_pair, int k, uint8_t* hq, uint8_t* hs,
+                            hipStream_t s);
+hipError_t launch_down_decode(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
+                              const uint8_t* hs, const int32_t* offsets, float* O,
+                              hipStream_t s);
+size_t prefill_tile_bytes(long P, int E);
+hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
+                             const uint8_t* xs, const int32_t* offsets,
+                             const int32_t* sorted_pair, int T, int k, uint8_t* hq, uint8_t* hs,
+                             void* tile_ws, hipStream_t s);
+hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
+                               const uint8_t* hs, const int32_t* offsets, int T, int k, float* O,
+                               void* tile_ws, hipStream_t s);
+hipError_t launch_combine(const float* O, const float* gates, const int32_t* pair_pos, int T,
+                          int k, int H, float* y, hipStream_t s);
+
+}  // namespace moe

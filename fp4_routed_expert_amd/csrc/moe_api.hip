@@ -1,0 +1,272 @@
+// C ABI of the library (declared in include/moe_fp4.h): host-side argument
+// checks, workspace carving and path selection.  Every check runs before any
+// launch, so a failing call enqueues nothing and touches no output.
+#include "common.h"
+#include "../../include/moe_fp4.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+moe_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+
+// Common checks of (T, E, k): negative or zero sizes are invalid, shapes
+// outside the kernels' coverage unsupported.
+moe_status_t check_tek(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > kMaxE || k > kMaxK || k > E) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t check_hi(int32_t H, int32_t I) {
+  if (H < 1 || I < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)H > (1 << 20) || (int64_t)I > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t check_weights(const moe_fp4_weights_t* w) {
+  if (!w || !w->packed) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->layout_version != MOE_FP4_LAYOUT_VERSION) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->E < 1 || w->E > kMaxE) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_hi(w->H, w->I);
+  if (st != MOE_OK) return st;
+  if (!aligned(w->packed, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->packed_bytes < PackedLayout(w->E, w->H, w->I).total) return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+// Path choice from host-known sizes only.  0 = decode, 1 = prefill, -1 = bad flags.
+int select_path(int64_t P, int E, uint32_t flags) {
+  const bool fd = flags & MOE_FLAG_FORCE_DECODE, fp = flags & MOE_FLAG_FORCE_PREFILL;
+  if ((flags & ~(MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_PREFILL)) != 0) return -1;
+  if (fd && fp) return -1;
+  if (fd) return 0;
+  if (fp) return 1;
+  return P <= 16 * (int64_t)E ? 0 : 1;
+}
+
+size_t stage_ws_bytes(int32_t T, int32_t k, int32_t E) {
+  return align256(prefill_tile_bytes((long)T * k, E));
+}
+
+struct FwdCarve {
+  size_t hq, hs, O, stage, total;
+};
+
+FwdCarve carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+  const size_t P = (size_t)T * (size_t)k;
+  FwdCarve c;
+  c.hq = 0;
+  c.hs = align256(c.hq + P * I);
+  c.O = align256(c.hs + P * (I / 32));
+  c.stage = align256(c.O + P * H * sizeof(float));
+  c.total = align256(c.stage + stage_ws_bytes(T, k, E));
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                            int32_t* topk_ids, float* topk_gates, hipStream_t stream) {
+  moe_status_t st = check_tek(T, E, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_gates) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_gates, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_route_topk(logits, T, E, k, topk_ids, topk_gates, stream));
+}
+
+size_t moe_sort_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
+  if (check_tek(T, E, k) != MOE_OK) return 0;
+  return align256(sort_workspace_bytes(T, E, k));
+}
+
+moe_status_t moe_sort_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
+                              int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  moe_status_t st = check_tek(T, E, k);
+  if (st != MOE_OK) return st;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = moe_sort_permute_workspace_size(T, E, k);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  // T == 0 still defines counts = 0 and offsets = 0 (the small kernel writes them)
+  return hip_status(launch_sort_permute(topk_ids, T, E, k, expert_counts, expert_offsets,
+                                        sorted_pair, pair_pos, workspace, stream));
+}
+
+moe_status_t moe_quant_act_mxfp8(const uint16_t* x_bf16, int32_t M, int32_t K, uint8_t* q,
+                                 uint8_t* s, hipStream_t stream) {
+  if (M < 0 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (K % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (!x_bf16 || !q || !s) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)M * K / 8 >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quant_mxfp8(x_bf16, M, K, q, s, stream));
+}
+
+size_t moe_fp4_packed_weight_bytes(int32_t E, int32_t H, int32_t I) {
+  if (E < 1 || E > kMaxE || check_hi(H, I) != MOE_OK) return 0;
+  return PackedLayout(E, H, I).total;
+}
+
+moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1, const uint8_t* w3,
+                                     const uint8_t* s3, const uint8_t* w2, const uint8_t* s2,
+                                     int32_t E, int32_t H, int32_t I, void* packed,
+                                     size_t packed_bytes, moe_fp4_weights_t* desc,
+                                     hipStream_t stream) {
+  if (E < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  moe_status_t st = check_hi(H, I);
+  if (st != MOE_OK) return st;
+  if (!w1 || !s1 || !w3 || !s3 || !w2 || !s2 || !packed || !desc) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) || !aligned(packed, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const PackedLayout L(E, H, I);
+  if (packed_bytes < L.total) return MOE_ERR_INVALID_ARGUMENT;
+  st = hip_status(launch_prepack(w1, s1, w3, s3, w2, s2, L, static_cast<uint8_t*>(packed), stream));
+  if (st != MOE_OK) return st;
+  desc->E = E;
+  desc->H = H;
+  desc->I = I;
+  desc->layout_version = MOE_FP4_LAYOUT_VERSION;
+  desc->packed = packed;
+  desc->packed_bytes = packed_bytes;
+  return MOE_OK;
+}
+
+size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E) {
+  if (check_tek(T, E, k) != MOE_OK) return 0;
+  return stage_ws_bytes(T, k, E);
+}
+
+moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, const uint8_t* xs,
+                               const int32_t* expert_offsets, const int32_t* sorted_pair,
+                               int32_t T, int32_t k, uint8_t* hq, uint8_t* hs, void* workspace,
+                               size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+  moe_status_t st = check_weights(w);
+  if (st != MOE_OK) return st;
+  st = check_tek(T, w->E, k);
+  if (st != MOE_OK) return st;
+  const int path = select_path((int64_t)T * k, w->E, flags);
+  if (path < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!xq || !xs || !expert_offsets || !sorted_pair || !hq || !hs) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(xq, 16) || !aligned(hq, 16) || !aligned(xs, 4) || !aligned(hs, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < stage_ws_bytes(T, k, w->E)) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  const PackedLayout L(w->E, w->H, w->I);
+  const uint8_t* pk = static_cast<const uint8_t*>(w->packed);
+  if (path == 1)
+    return hip_status(launch_up_prefill(pk, L, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs,
+                                        workspace, stream));
+  return hip_status(launch_up_decode(pk, L, xq, xs, expert_offsets, sorted_pair, k, hq, hs, stream));
+}
+
+moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, const uint8_t* hs,
+                                 const int32_t* expert_offsets, int32_t T, int32_t k, float* O,
+                                 void* workspace, size_t workspace_bytes, uint32_t flags,
+                                 hipStream_t stream) {
+  moe_status_t st = check_weights(w);
+  if (st != MOE_OK) return st;
+  st = check_tek(T, w->E, k);
+  if (st != MOE_OK) return st;
+  const int path = select_path((int64_t)T * k, w->E, flags);
+  if (path < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!hq || !hs || !expert_offsets || !O) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(hq, 16) || !aligned(O, 16) || !aligned(hs, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < stage_ws_bytes(T, k, w->E)) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  const PackedLayout L(w->E, w->H, w->I);
+  const uint8_t* pk = static_cast<const uint8_t*>(w->packed);
+  if (path == 1)
+    return hip_status(launch_down_prefill(pk, L, hq, hs, expert_offsets, T, k, O, workspace, stream));
+  return hip_status(launch_down_decode(pk, L, hq, hs, expert_offsets, O, stream));
+}
+
+moe_status_t moe_combine(const float* O, const float* topk_gates, const int32_t* pair_pos,
+                         int32_t T, int32_t k, int32_t H, float* y, hipStream_t stream) {
+  if (T < 0 || k < 1 || H < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > kMaxK || H % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!O || !topk_gates || !pair_pos || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(O, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_combine(O, topk_gates, pair_pos, T, k, H, y, stream));
+}
+
+size_t moe_fp4_forward_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                      uint32_t flags) {
+  (void)flags;
+  if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
+  return carve(T, k, E, H, I).total;
+}
+
+moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w, const uint8_t* xq,
+                                     const uint8_t* xs, const float* topk_gates,
+                                     const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                     const int32_t* pair_pos, int32_t T, int32_t k, float* y,
+                                     void* workspace, size_t workspace_bytes, uint32_t flags,
+                                     hipStream_t stream) {
+  moe_status_t st = check_weights(w);
+  if (st != MOE_OK) return st;
+  st = check_tek(T, w->E, k);
+  if (st != MOE_OK) return st;
+  if (select_path((int64_t)T * k, w->E, flags) < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!xq || !xs || !topk_gates || !expert_offsets || !sorted_pair || !pair_pos || !y)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(xq, 16) || !aligned(y, 16) || !aligned(xs, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  const FwdCarve c = carve(T, k, w->E, w->H, w->I);
+  if (!workspace || workspace_bytes < c.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* hq = ws + c.hq;
+  uint8_t* hs = ws + c.hs;
+  float* O = reinterpret_cast<float*>(ws + c.O);
+  void* stage = ws + c.stage;
+  const size_t stage_bytes = c.total - c.stage;
+  st = moe_fp4_expert_up(w, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs, stage,
+                         stage_bytes, flags, stream);
+  if (st != MOE_OK) return st;
+  st = moe_fp4_expert_down(w, hq, hs, expert_offsets, T, k, O, stage, stage_bytes, flags, stream);
+  if (st != MOE_OK) return st;
+  return moe_combine(O, topk_gates, pair_pos, T, k, w->H, y, stream);
+}
+
+}  // extern "C"

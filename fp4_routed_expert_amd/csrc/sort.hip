@@ -1,0 +1,165 @@
+// Expert sort / permute of the (token, slot) pairs: counting sort by expert.
+//
+// Counts come from LDS integer atomics (order-free, so exact and deterministic).
+// Positions never come from atomics: a pair's rank among the pairs of its expert
+// is the number of earlier pairs with the same expert, computed from wavefront
+// ballots (equal-id lane masks) and a per-wave table in LDS, so the order
+// inside each expert is ascending pair index -- a stable sort, as required by
+// pwwt.cn review section 4.2 (no unstable sorting; ties by expert id).
+//
+// P <= kChunk pairs: one workgroup does histogram, scan and scatter.
+// Larger P: (1) per-chunk histograms, (2) one workgroup scans them in
+// (expert, chunk) order, (3) each chunk scatters from its own base.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;           // 4 waves
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 4096;            // pairs per workgroup
+constexpr int kMaxE = 1024;
+
+// Stable scatter of pairs [p0, p1) given base[e] = first free sorted position
+// of expert e for this range.  table is [kWaves][E] of zeros on entry and exit.
+__device__ void stable_scatter(const int32_t* __restrict__ ids, int p0, int p1, int E, int* base,
+                               int* table, int32_t* __restrict__ sorted_pair,
+                               int32_t* __restrict__ pair_pos) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c = p0; c < p1; c += kThreads) {
+    const int p = c + tid;
+    const bool valid = p < p1;
+    const int id = valid ? ids[p] : kMaxE;  // sentinel outside [0, E)
+    // lanes holding the same id: intersect the 11 bit-planes of the ids
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+      const uint64_t ones = __ballot((id >> b) & 1);
+      same &= ((id >> b) & 1) ? ones : ~ones;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int cnt = __popcll(same);
+    const bool leader = valid && rank == 0;
+    if (leader) table[w * E + id] = cnt;
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int i = 0; i < w; ++i) pre += table[i * E + id];
+      const int pos = base[id] + pre + rank;
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&base[id], cnt);  // integer: order-free
+      table[w * E + id] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void sort_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_pos) {
+  __shared__ int hist[kMaxE];
+  __shared__ int table[kWaves * kMaxE];
+  __shared__ int wave_tot[kWaves];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) hist[e] = 0;
+  for (int i = tid; i < kWaves * E; i += kThreads) table[i] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kThreads) atomicAdd(&hist[ids[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) counts[e] = hist[e];
+  __syncthreads();
+  const int total = block_exclusive_scan256(hist, E, wave_tot);
+  for (int e = tid; e < E; e += kThreads) offsets[e] = hist[e];
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  stable_scatter(ids, 0, P, E, hist, table, sorted_pair, pair_pos);
+}
+
+__global__ __launch_bounds__(kThreads) void sort_hist_kernel(const int32_t* __restrict__ ids,
+                                                             int P, int E,
+                                                             int32_t* __restrict__ chunk_counts) {
+  __shared__ int hist[kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kChunk, p1 = min(P, p0 + kChunk);
+  for (int p = p0 + tid; p < p1; p += kThreads) atomicAdd(&hist[ids[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) chunk_counts[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// chunk_counts[b][e] -> first sorted position of chunk b's pairs of expert e.
+__global__ __launch_bounds__(kThreads) void sort_scan_kernel(int nchunks, int P, int E,
+                                                             int32_t* __restrict__ chunk_counts,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int tot[kMaxE];
+  __shared__ int wave_tot[kWaves];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) {
+    int run = 0;
+    for (int b = 0; b < nchunks; ++b) {
+      const int c = chunk_counts[(size_t)b * E + e];
+      chunk_counts[(size_t)b * E + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan256(tot, E, wave_tot);
+  for (int e = tid; e < E; e += kThreads) {
+    offsets[e] = tot[e];
+    for (int b = 0; b < nchunks; ++b) chunk_counts[(size_t)b * E + e] += tot[e];
+  }
+  if (tid == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(kThreads) void sort_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ chunk_base,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
+  __shared__ int base[kMaxE];
+  __shared__ int table[kWaves * kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) base[e] = chunk_base[(size_t)blockIdx.x * E + e];
+  for (int i = tid; i < kWaves * E; i += kThreads) table[i] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kChunk, p1 = min(P, p0 + kChunk);
+  stable_scatter(ids, p0, p1, E, base, table, sorted_pair, pair_pos);
+}
+
+}  // namespace
+
+size_t sort_workspace_bytes(int T, int E, int k) {
+  const long P = (long)T * k;
+  const long nchunks = (P + kChunk - 1) / kChunk;
+  return nchunks <= 1 ? 0 : (size_t)nchunks * E * sizeof(int32_t);
+}
+
+hipError_t launch_sort_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                               void* ws, hipStream_t s) {
+  const int P = T * k;
+  const int nchunks = (P + kChunk - 1) / kChunk;
+  if (nchunks <= 1) {
+    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(kThreads), 0, s, ids, P, E, counts,
+                       offsets, sorted_pair, pair_pos);
+    return hipGetLastError();
+  }
+  int32_t* chunk_counts = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(sort_hist_kernel, dim3(nchunks), dim3(kThreads), 0, s, ids, P, E,
+                     chunk_counts);
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(kThreads), 0, s, nchunks, P, E,
+                     chunk_counts, counts, offsets);
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3(nchunks), dim3(kThreads), 0, s, ids, P, E,
+                     chunk_counts, sorted_pair, pair_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,210 @@
+/*
+ * moe_fp4.h -- C ABI of the MI355X (gfx950) FP4 routed-expert MoE layer.
+ *
+ * The layer: top-k routing over router logits, a stable expert sort/permute
+ * of the (token, slot) pairs, MXFP8 quantisation of the activations, the
+ * gate/up (W1/W3) and down (W2) grouped GEMMs over packed 4-bit e2m1 weights
+ * with one E8M0 scale per 32 elements along K, SwiGLU between them, and a
+ * gate-weighted combine back to token order.  The pages name this "FP4 routed
+ * mixture-of-experts computation" and trace the wrong outputs of the first
+ * fast path to a routed-expert W2 layout mismatch repaired once at load time
+ * ("DeepSeek-V4-Flash on AMD gfx90a: Correctness Recovery and Inference
+ * Performance Engineering", abstract).
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers unless a comment says (host).  The caller
+ *    allocates and frees everything, including workspaces sized by the
+ *    *_workspace_size() queries and the packed-weight buffer.  The library
+ *    never allocates, frees or synchronises, and never copies device data to
+ *    the host, so a chain of calls can be captured in a HIP graph: launches
+ *    take device pointers and sizes only and read no host scalars mid-way
+ *    (the capture rule of the aijianwen.com MI300X log, HIP graph section).
+ *  - Every call only enqueues work on `stream`, in order.  MOE_OK means
+ *    "enqueued"; results are ready when the stream reaches that point.
+ *  - All argument checks run on the host before anything is enqueued.  On an
+ *    error nothing is enqueued and outputs are untouched.  Device data is not
+ *    validated: logits must be finite and expert ids must come from
+ *    moe_route_topk.
+ *  - Tensors are row-major and contiguous.  Byte tensors and x must be
+ *    16-byte aligned; the packed-weight buffer 256-byte aligned.
+ *  - Formats: e2m1 nibbles two per byte along K, the EVEN K index in the LOW
+ *    nibble; E8M0 scale code c means 2^(c-127); activations use OCP e4m3fn
+ *    (bias 7, max 448, 0x7F/0xFF NaN) -- the dialect MI355X uses (aijianwen.com
+ *    MI300X log, FP8 section); x is bf16, logits/gates/y are fp32.
+ *  - Determinism: the same inputs give bitwise-identical outputs, run to run.
+ *    No floating-point atomics anywhere; reductions go in a fixed order
+ *    (pwwt.cn review, section 4.2).
+ *  - Supported shapes: 1 <= k <= min(E, 32), E <= 1024, H % 128 == 0,
+ *    I % 128 == 0, 0 <= T, T*k < 2^31.  T == 0 is a no-op.  Anything else
+ *    returns MOE_ERR_UNSUPPORTED (or MOE_ERR_INVALID_ARGUMENT for negative
+ *    sizes and null pointers).
+ *  - Re-entrant; outputs must not alias inputs.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative or inconsistent size, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,      /* well-formed but outside the supported shapes above */
+  MOE_ERR_WORKSPACE = 3,        /* workspace smaller than the matching *_workspace_size() */
+  MOE_ERR_HIP = 4               /* a HIP launch failed; see moe_last_hip_error() */
+} moe_status_t;
+
+/* Static string naming a status code (never NULL). */
+const char* moe_status_string(moe_status_t status);
+
+/* The hipError_t of the last failed launch on the calling thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* Layout version of moe_fp4_prepack_weights' output. */
+#define MOE_FP4_LAYOUT_VERSION 1u
+
+/*
+ * Top-k routing (step 1 of the layer).
+ * For each token t the k experts with the largest logits, ties to the LOWER
+ * expert index (a fixed tie-break by expert id: pwwt.cn review, section 4.1
+ * table row "MoE routing top-k", and section 4.2), compared as fp32 values
+ * (-0 equals +0).  Slot j = 0 holds the largest.  Gates are a softmax over the
+ * k selected logits: g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), in fp32.
+ *   logits     [T, E] fp32, finite
+ *   topk_ids   [T, k] int32 (out)
+ *   topk_gates [T, k] fp32  (out)
+ */
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                            int32_t* topk_ids, float* topk_gates, hipStream_t stream);
+
+/*
+ * Expert sort / permute (step 2; "retuned expert sorting" in the abstract).
+ * Pairs p = t*k + j.  expert_counts[e] = #pairs routed to e; expert_offsets
+ * is the exclusive prefix sum with expert_offsets[E] = T*k; sorted_pair lists
+ * the pairs grouped by expert in ascending e, and ascending p inside each
+ * group (stable: pwwt.cn review, section 4.2 forbids unstable sorting);
+ * pair_pos is its inverse (pair_pos[sorted_pair[s]] = s).
+ *   topk_ids       [T, k] int32, each in [0, E)
+ *   expert_counts  [E] int32 (out);  expert_offsets [E+1] int32 (out)
+ *   sorted_pair    [T*k] int32 (out); pair_pos      [T*k] int32 (out)
+ *   workspace      >= moe_sort_permute_workspace_size(T, E, k) bytes, 256-aligned
+ */
+size_t moe_sort_permute_workspace_size(int32_t T, int32_t E, int32_t k);
+moe_status_t moe_sort_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
+                              int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * MXFP8 activation quantisation (step 3; the pages' gfx90a path used INT8
+ * activation quantisation, the abstract).  For each row and each block of 32
+ * consecutive elements: X = floor(log2(max|v|)) - 8 (8 = largest e4m3
+ * exponent), X = -127 for an all-zero block, X clamped to [-127, 127]; scale
+ * code X + 127; element code = v * 2^-X rounded to e4m3fn, nearest, ties to
+ * even, saturating to +-448, sign kept (so -tiny -> 0x80).
+ *   x_bf16 [M, K] bf16 bit patterns; K % 32 == 0
+ *   q      [M, K] e4m3fn bytes (out);  s [M, K/32] E8M0 codes (out)
+ */
+moe_status_t moe_quant_act_mxfp8(const uint16_t* x_bf16, int32_t M, int32_t K,
+                                 uint8_t* q, uint8_t* s, hipStream_t stream);
+
+/*
+ * Load-time weight prepack, which also fixes the W2 layout once (the abstract:
+ * the output permutation was identified and the weight layout repaired at
+ * load time).  Canonical inputs (device):
+ *   w1, w3 [E, I, H/2] packed e2m1;  s1, s3 [E, I, H/32] E8M0
+ *   w2     [E, H, I/2] packed e2m1;  s2     [E, H, I/32] E8M0
+ * Output: `packed` (device, >= moe_fp4_packed_weight_bytes(E, H, I) bytes,
+ * 256-byte aligned) in the kernels' tile order, and `desc` (host) which the
+ * forward calls take.  The caller keeps `packed` alive and unmodified while
+ * `desc` is in use; the canonical inputs may be freed once the stream has
+ * passed this call.
+ */
+typedef struct moe_fp4_weights {
+  int32_t E, H, I;
+  uint32_t layout_version;
+  const void* packed;   /* device */
+  size_t packed_bytes;
+} moe_fp4_weights_t;
+
+size_t moe_fp4_packed_weight_bytes(int32_t E, int32_t H, int32_t I);
+moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1,
+                                     const uint8_t* w3, const uint8_t* s3,
+                                     const uint8_t* w2, const uint8_t* s2,
+                                     int32_t E, int32_t H, int32_t I,
+                                     void* packed, size_t packed_bytes,
+                                     moe_fp4_weights_t* desc, hipStream_t stream);
+
+/* Path selection for the expert GEMMs.  By default the host picks from the
+ * host-known T*k and E only (never from device counts): the weight-streaming
+ * decode path when T*k <= 16*E, the MFMA-tiled prefill path otherwise.  The
+ * flags force one path (both compute the same function). */
+#define MOE_FLAG_FORCE_DECODE 1u
+#define MOE_FLAG_FORCE_PREFILL 2u
+
+/*
+ * Expert gate/up GEMM + SwiGLU + MXFP8 of h (steps 4-5), in sorted order.
+ * For each expert e and each sorted position s in [off[e], off[e+1]) with
+ * token t = sorted_pair[s] / k:
+ *   G[s,i] = sum_h x[t,h] W1[e,i,h],  U[s,i] = sum_h x[t,h] W3[e,i,h]
+ * (MXFP8 x times FP4 W, fp32 accumulation), h = G / (1 + e^-G) * U in fp32,
+ * then hq/hs = MXFP8 of h per 32 along I (the rule of moe_quant_act_mxfp8).
+ *   xq [T, H], xs [T, H/32] from moe_quant_act_mxfp8
+ *   expert_offsets [E+1], sorted_pair [T*k] from moe_sort_permute
+ *   hq [T*k, I] (out), hs [T*k, I/32] (out), rows in sorted order
+ *   workspace >= moe_fp4_stage_workspace_size(T, k, E)
+ */
+size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E);
+moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w /*(host)*/,
+                               const uint8_t* xq, const uint8_t* xs,
+                               const int32_t* expert_offsets, const int32_t* sorted_pair,
+                               int32_t T, int32_t k, uint8_t* hq, uint8_t* hs,
+                               void* workspace, size_t workspace_bytes,
+                               uint32_t flags, hipStream_t stream);
+
+/*
+ * Expert down GEMM (step 6): O[s,r] = sum_i h[s,i] W2[e,r,i], fp32, rows in
+ * sorted order.
+ *   hq [T*k, I], hs [T*k, I/32] from moe_fp4_expert_up
+ *   O  [T*k, H] fp32 (out)
+ */
+moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w /*(host)*/,
+                                 const uint8_t* hq, const uint8_t* hs,
+                                 const int32_t* expert_offsets, int32_t T, int32_t k,
+                                 float* O, void* workspace, size_t workspace_bytes,
+                                 uint32_t flags, hipStream_t stream);
+
+/*
+ * Gate-weighted combine (step 7): y[t,r] = sum_{j=0..k-1, in this order}
+ * gates[t,j] * O[pair_pos[t*k+j], r], fp32, no atomics.
+ *   O [T*k, H] fp32; topk_gates [T, k]; pair_pos [T*k]; y [T, H] fp32 (out)
+ *   H % 4 == 0
+ */
+moe_status_t moe_combine(const float* O, const float* topk_gates, const int32_t* pair_pos,
+                         int32_t T, int32_t k, int32_t H, float* y, hipStream_t stream);
+
+/*
+ * Steps 4-7 in one call: expert_up -> expert_down -> combine, with hq, hs, O
+ * and the tile map held in `workspace`
+ * (>= moe_fp4_forward_workspace_size(T, k, E, H, I, flags) bytes, 256-aligned).
+ *   y [T, H] fp32 (out, overwritten)
+ */
+size_t moe_fp4_forward_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                      uint32_t flags);
+moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w /*(host)*/,
+                                     const uint8_t* xq, const uint8_t* xs, const float* topk_gates,
+                                     const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                     const int32_t* pair_pos, int32_t T, int32_t k,
+                                     float* y, void* workspace, size_t workspace_bytes,
+                                     uint32_t flags, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

@@ -1,0 +1,126 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments before it touches the GPU (no device
+here: every case below must return its error code without a HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_routed_expert_amd import _lib
+
+L = None
+
+
+def setup_module():
+    global L
+    if not os.path.exists(_lib.SO_PATH):
+        from fp4_routed_expert_amd import build
+        build.build()
+    L = _lib.lib()
+
+
+def declared_functions():
+    text = open(_lib.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) == 14, names
+    so = ctypes.CDLL(_lib.SO_PATH)
+    for n in names:
+        assert hasattr(so, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_status_strings():
+    assert _lib.status_string(0) == "MOE_OK"
+    assert _lib.status_string(3) == "MOE_ERR_WORKSPACE"
+    assert L.moe_last_hip_error() == 0
+
+
+A = ctypes.c_void_p(1 << 20)        # 256-aligned stand-ins: never dereferenced on error paths
+MIS = ctypes.c_void_p((1 << 20) + 4)
+NUL = ctypes.c_void_p(0)
+INV, UNS, WSE = _lib.MOE_ERR_INVALID_ARGUMENT, _lib.MOE_ERR_UNSUPPORTED, _lib.MOE_ERR_WORKSPACE
+
+
+def test_route_argument_errors():
+    assert L.moe_route_topk(A, -1, 8, 2, A, A, NUL) == INV
+    assert L.moe_route_topk(A, 4, 0, 1, A, A, NUL) == INV
+    assert L.moe_route_topk(A, 4, 8, 0, A, A, NUL) == INV
+    assert L.moe_route_topk(A, 4, 8, 9, A, A, NUL) == UNS        # k > E
+    assert L.moe_route_topk(A, 4, 1025, 2, A, A, NUL) == UNS     # E > 1024
+    assert L.moe_route_topk(A, 4, 64, 33, A, A, NUL) == UNS      # k > 32
+    assert L.moe_route_topk(NUL, 4, 8, 2, A, A, NUL) == INV
+    assert L.moe_route_topk(A, 0, 8, 2, NUL, NUL, NUL) == 0       # T = 0: no-op
+    assert L.moe_route_topk(A, 1 << 27, 64, 16, A, A, NUL) == UNS  # T*k >= 2^31
+
+
+def test_sort_argument_errors():
+    assert L.moe_sort_permute_workspace_size(16, 8, 2) == 0       # one chunk: no workspace
+    need = L.moe_sort_permute_workspace_size(16384, 256, 8)
+    assert need == 32 * 256 * 4
+    assert L.moe_sort_permute(A, 16384, 256, 8, A, A, A, A, A, need - 1, NUL) == WSE
+    assert L.moe_sort_permute(A, 16384, 256, 8, A, A, A, A, NUL, need, NUL) == WSE
+    assert L.moe_sort_permute(A, 16384, 256, 8, A, A, A, A, MIS, need, NUL) == INV
+    assert L.moe_sort_permute(A, 4, 8, 2, NUL, A, A, A, NUL, 0, NUL) == INV
+
+
+def test_quant_argument_errors():
+    assert L.moe_quant_act_mxfp8(A, 4, 48, A, A, NUL) == UNS       # K % 32
+    assert L.moe_quant_act_mxfp8(A, -1, 64, A, A, NUL) == INV
+    assert L.moe_quant_act_mxfp8(MIS, 4, 64, A, A, NUL) == INV
+    assert L.moe_quant_act_mxfp8(A, 0, 64, NUL, NUL, NUL) == 0
+
+
+def test_packed_bytes_and_prepack_errors():
+    nb = L.moe_fp4_packed_weight_bytes(256, 7168, 2048)
+    nibbles = 256 * 3 * 7168 * 2048 // 2
+    scales = 256 * 3 * 7168 * 2048 // 32
+    assert nibbles + scales <= nb <= nibbles + scales + (1 << 20)
+    assert L.moe_fp4_packed_weight_bytes(8, 200, 128) == 0        # H % 128
+    desc = _lib.MoeFp4Weights()
+    nb0 = L.moe_fp4_packed_weight_bytes(8, 256, 128)
+    assert L.moe_fp4_prepack_weights(A, A, A, A, A, A, 8, 256, 96, A, nb0, ctypes.byref(desc), NUL) == UNS
+    assert L.moe_fp4_prepack_weights(A, A, A, A, A, A, 8, 256, 128, A, nb0 - 1, ctypes.byref(desc), NUL) == INV
+    assert L.moe_fp4_prepack_weights(A, A, A, A, A, A, 8, 256, 128, MIS, nb0, ctypes.byref(desc), NUL) == INV
+    assert L.moe_fp4_prepack_weights(A, A, A, A, A, A, 0, 256, 128, A, nb0, ctypes.byref(desc), NUL) == INV
+
+
+def _desc(E=8, H=256, I=128, version=1):
+    d = _lib.MoeFp4Weights()
+    d.E, d.H, d.I, d.layout_version = E, H, I, version
+    d.packed = 1 << 20
+    d.packed_bytes = L.moe_fp4_packed_weight_bytes(E, H, I)
+    return d
+
+
+def test_forward_argument_errors():
+    d = _desc()
+    ws = L.moe_fp4_forward_workspace_size(16, 2, 8, 256, 128, 0)
+    assert ws >= 32 * 128 + 32 * 4 + 32 * 256 * 4
+    fwd = L.moe_fp4_grouped_forward
+    assert fwd(ctypes.byref(_desc(version=7)), A, A, A, A, A, A, 16, 2, A, A, ws, 0, NUL) == INV
+    assert fwd(ctypes.byref(d), A, A, A, A, A, A, 16, 2, A, A, ws, 3, NUL) == INV  # both paths forced
+    assert fwd(ctypes.byref(d), A, A, A, A, A, A, 16, 2, A, A, ws - 1, 0, NUL) == WSE
+    assert fwd(ctypes.byref(d), A, A, A, A, A, A, 16, 9, A, A, ws, 0, NUL) == UNS  # k > E
+    assert fwd(ctypes.byref(d), NUL, A, A, A, A, A, 16, 2, A, A, ws, 0, NUL) == INV
+    assert fwd(ctypes.byref(d), A, A, A, A, A, A, 0, 2, A, A, 0, 0, NUL) == 0      # T = 0
+    small = _desc()
+    small.packed_bytes -= 1
+    assert fwd(ctypes.byref(small), A, A, A, A, A, A, 16, 2, A, A, ws, 0, NUL) == INV
+    up = L.moe_fp4_expert_up
+    sws = L.moe_fp4_stage_workspace_size(16, 2, 8)
+    assert up(ctypes.byref(d), A, A, A, A, 16, 2, A, A, A, sws - 1, 0, NUL) == WSE
+    assert L.moe_combine(A, A, A, 4, 2, 250, A, NUL) == UNS       # H % 4
+    assert L.moe_combine(A, A, A, 4, 0, 256, A, NUL) == INV
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "SO_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
