@@ -36,6 +36,56 @@ def weight_bytes_per_expert(H: int, I: int, mats: int) -> float:
     return mats * H * I * (0.5 + 1.0 / 32)
 
 
+def rocprof_summary(paths) -> str:
+    """Markdown summary of rocprofv3 CSV outputs (kernel stats and, if present,
+    per-dispatch counters averaged per kernel)."""
+    import csv
+    import glob
+    out = []
+    files = []
+    for p in paths:
+        files += glob.glob(os.path.join(p, "**", "*.csv"), recursive=True) if os.path.isdir(p) else [p]
+    for f in sorted(files):
+        rows = list(csv.DictReader(open(f)))
+        if not rows:
+            continue
+        if f.endswith("kernel_stats.csv"):
+            out.append(f"### kernel stats ({os.path.basename(f)})\n")
+            out.append("| kernel | calls | avg us | min us | max us | total ms | % |")
+            out.append("|---|---|---|---|---|---|---|")
+            for r in rows:
+                name = r["Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+                out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                           f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                           f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+            out.append("")
+        elif f.endswith("counter_collection.csv"):
+            agg = {}
+            for r in rows:
+                name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+                key = (name, r["Counter_Name"])
+                agg.setdefault(key, []).append(float(r["Counter_Value"]))
+            out.append(f"### counters per dispatch ({os.path.basename(f)})\n")
+            out.append("| kernel | counter | dispatches | mean per dispatch |")
+            out.append("|---|---|---|---|")
+            for (name, cn), v in sorted(agg.items()):
+                out.append(f"| {name} | {cn} | {len(v)} | {np.mean(v):.1f} |")
+            out.append("")
+    return "\n".join(out)
+
+
+def copy_calibration(reps: int = 20):
+    """A plain device copy of 1 GiB, `reps` times: 1 GiB read + 1 GiB written per
+    dispatch, the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(name: str, budget_s: float):
     import oracle
     import synth
@@ -64,7 +114,14 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="1 = force decode path, 2 = force prefill path")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 = skip")
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 20 plain 1 GiB device copies (HBM counter calibration)")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="PATH",
+                    help="print a markdown summary of rocprofv3 CSV outputs and exit")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer's multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
@@ -142,6 +199,19 @@ def main():
     b_up = used * weight_bytes_per_expert(H, I, 2) + T * H * (1 + 1 / 32) + P * I * (1 + 1 / 32)
     up_gbs = b_up / (up_ms * 1e-3) / 1e9
     flops = 6.0 * H * I * P
+    up_flops = 4.0 * H * I * P
+    prefill = args.flags == 2 or (args.flags == 0 and P > 16 * E)
+    if prefill:
+        achieved = up_flops / (up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "up_prefill_kernel (gate/up GEMM + SwiGLU + MXFP8)",
+                "achieved": achieved, "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_FP8_PEAK_TFLOPS, "traffic": None,
+                "alg_flops_per_launch": up_flops, "avg_launch_us": up_ms * 1e3}
+    else:
+        roof = {"bound": "hbm", "kernel": "up_decode_kernel (gate/up GEMM + SwiGLU + MXFP8)",
+                "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": up_gbs / HBM_PEAK_GBS, "traffic": None,
+                "alg_bytes_per_launch": b_up, "avg_launch_us": up_ms * 1e3}
     line = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -161,11 +231,10 @@ def main():
         "layer_hbm_tbps": b_layer / (ms_per_step * 1e-3) / 1e12,
         "layer_hbm_frac": b_layer / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_mfma_frac_fp8": flops / (ms_per_step * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
-        "roofline": {"bound": "hbm", "kernel": "up_decode_kernel (gate/up GEMM + SwiGLU + MXFP8)",
-                     "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": up_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "alg_bytes_per_launch": b_up, "avg_launch_us": up_ms * 1e3},
+        "roofline": roof,
     }
+    if args.copy_calibration:
+        copy_calibration()
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
     else:

@@ -92,51 +92,51 @@ __device__ __forceinline__ int block_exclusive_scan256(int* a, int n, int* wave_
 // Every weight tile is the B operand of one v_mfma_scale_f32_16x16x128_f8f6f4:
 // 16 output rows x 128 K, 1 KiB, stored in lane order: lane l holds row
 // (l & 15) and K elements [32*(l >> 4), +32) as 16 consecutive bytes (even K
-// in the low nibble), i.e. exactly one 32-element scale block per lane.
+// in the low nibble), i.e. exactly one 32-element scale block per lane (the B
+// operand's lane layout and its per-lane scale were measured on gfx950).
 //
 // Region UPW (gate/up weights): per expert e, per 32-row group q of I, per
-// K-step j of H/128: 4 tiles of 1 KiB = [W1 rows 32q..+16, W1 rows 32q+16..+16,
-//                                        W3 rows 32q..+16, W3 rows 32q+16..+16]
-// Region UPS (their scales): per (e, q, jg = j/4): 4 tiles x 64 lanes x 4 B;
-//   byte b of a lane's dword is that lane's scale in K-step 4*jg + b.
+//   K-step j of H/128: 4 tiles of 1 KiB = [W1 rows 32q..+16, W1 rows 32q+16..+16,
+//                                          W3 rows 32q..+16, W3 rows 32q+16..+16]
+// Region UPS (their scales): per (e, q, j): 64 lanes x 4 B; byte t of lane l's
+//   dword is the E8M0 scale of lane l's block in tile t.
 // Region DNW (down weights): per expert e, per 32-row group q2 of H, per
 //   K-step j2 of I/128: 2 tiles = [W2 rows 32q2..+16, 32q2+16..+16].
-// Region DNS (their scales): per (e, q2, jg2): 2 tiles x 64 lanes x 4 B.
+// Region DNS (their scales): per (e, q2, j2): 64 lanes x 2 B (byte t = tile t).
 struct PackedLayout {
   int E, H, I;
-  int J, JG;    // gate/up K-steps (H/128) and scale groups ceil(J/4)
-  int J2, JG2;  // down K-steps (I/128) and scale groups
+  int J;   // gate/up K-steps (H/128)
+  int J2;  // down K-steps (I/128)
   size_t upw_off, ups_off, dnw_off, dns_off, total;
 
   __host__ __device__ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
   __host__ __device__ PackedLayout(int E_, int H_, int I_) : E(E_), H(H_), I(I_) {
     J = H / 128;
-    JG = (J + 3) / 4;
     J2 = I / 128;
-    JG2 = (J2 + 3) / 4;
     const size_t upw = (size_t)E * (I / 32) * J * 4096;
-    const size_t ups = (size_t)E * (I / 32) * JG * 1024;
+    const size_t ups = (size_t)E * (I / 32) * J * 256;
     const size_t dnw = (size_t)E * (H / 32) * J2 * 2048;
-    const size_t dns = (size_t)E * (H / 32) * JG2 * 512;
+    const size_t dns = (size_t)E * (H / 32) * J2 * 128;
     upw_off = 0;
     ups_off = align256(upw_off + upw);
     dnw_off = align256(ups_off + ups);
     dns_off = align256(dnw_off + dnw);
     total = align256(dns_off + dns);
   }
-  // byte offset of the 4 KiB gate/up block (e, q, j)
+  // byte offset of the 4 KiB gate/up block (e, q, j) and of its 256 B of scales
   __host__ __device__ size_t upw_block(int e, int q, int j) const {
     return upw_off + (((size_t)e * (I / 32) + q) * J + j) * 4096;
   }
-  __host__ __device__ size_t ups_block(int e, int q, int jg) const {
-    return ups_off + (((size_t)e * (I / 32) + q) * JG + jg) * 1024;
+  __host__ __device__ size_t ups_block(int e, int q, int j) const {
+    return ups_off + (((size_t)e * (I / 32) + q) * J + j) * 256;
   }
+  // byte offset of the 2 KiB down block (e, q2, j2) and of its 128 B of scales
   __host__ __device__ size_t dnw_block(int e, int q2, int j2) const {
     return dnw_off + (((size_t)e * (H / 32) + q2) * J2 + j2) * 2048;
   }
-  __host__ __device__ size_t dns_block(int e, int q2, int jg2) const {
-    return dns_off + (((size_t)e * (H / 32) + q2) * JG2 + jg2) * 512;
+  __host__ __device__ size_t dns_block(int e, int q2, int j2) const {
+    return dns_off + (((size_t)e * (H / 32) + q2) * J2 + j2) * 128;
   }
 };
 

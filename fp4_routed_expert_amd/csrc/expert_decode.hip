@@ -5,7 +5,9 @@
 // and streams those rows' packed tiles over the whole K range, its four waves
 // splitting K; each wave issues 128-bit loads of whole 1 KiB tiles (a tile is
 // contiguous in the packed layout, so a wave's load is one 1 KiB run) plus one
-// dword of four E8M0 scales per lane per four K-steps.  The dot products run on
+// dword per lane per K-step holding the four tiles' E8M0 scales.  Each wave
+// issues the loads of kBatch K-steps back to back before using them, so that
+// enough bytes are in flight per CU to cover HBM latency.  The dot products run on
 // the gfx950 scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, MXFP8 activations
 // as A, FP4 weights as B, one E8M0 scale per lane and operand), which applies
 // the block scales in hardware: the token rows are padded to 16, compute is far
@@ -18,7 +20,8 @@
 namespace moe {
 namespace {
 
-constexpr int kNW = 4;  // waves per workgroup, splitting K
+constexpr int kNW = 4;     // waves per workgroup, splitting K
+constexpr int kBatch = 4;  // K-steps whose loads a wave issues together
 
 // A operand (fp8) of the 16x16x128 scaled MFMA: lane l holds row l%16 and, for
 // g = l/16, K elements [16g, 16g+16) in bytes 0-15 and [64+16g, 64+16g+16) in
@@ -71,19 +74,35 @@ __global__ __launch_bounds__(kNW * 64) void up_decode_kernel(
     v4f acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int j = j0; j < j1; ++j) {
-      v8i a = valid ? load_a_fp8(arow + (size_t)j * 128) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      const int sa = valid ? (int)srow[j * 4] : 127;
-      const uint8_t* wj = wblk + (size_t)j * 4096;
-      uint4 b[4];
+    for (int j = j0; j < j1; j += kBatch) {
+      uint4 b[kBatch][4];
+      uint32_t sw[kBatch];
+      v8i a[kBatch];
+      int sa[kBatch];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
-      const uint32_t* sj = sblk + (size_t)(j >> 2) * 256;
-      const int sh = (j & 3) * 8;
+      for (int u = 0; u < kBatch; ++u) {
+        if (j + u < j1) {
+          const uint8_t* wj = wblk + (size_t)(j + u) * 4096;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int sb = (int)((sj[t * 64] >> sh) & 0xFFu);
-        acc[t] = mfma_fp8_fp4(a, widen_fp4(b[t]), acc[t], sa, sb);
+          for (int t = 0; t < 4; ++t) b[u][t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
+          sw[u] = sblk[(size_t)(j + u) * 64];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j + u < j1) {
+          a[u] = valid ? load_a_fp8(arow + (size_t)(j + u) * 128) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          sa[u] = valid ? (int)srow[(j + u) * 4] : 127;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j + u < j1) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[t] = mfma_fp8_fp4(a[u], widen_fp4(b[u][t]), acc[t], sa[u],
+                                  (int)((sw[u] >> (8 * t)) & 0xFFu));
+        }
       }
     }
 #pragma unroll
@@ -133,7 +152,7 @@ __global__ __launch_bounds__(kNW * 64) void down_decode_kernel(
   const int H = L.H, I = L.I, J2 = L.J2;
   const int j0 = (wave * J2) / kNW, j1 = ((wave + 1) * J2) / kNW;
   const uint8_t* wblk = packed + L.dnw_block(e, q2, 0) + lane * 16;
-  const uint32_t* sblk = reinterpret_cast<const uint32_t*>(packed + L.dns_block(e, q2, 0)) + lane;
+  const uint16_t* sblk = reinterpret_cast<const uint16_t*>(packed + L.dns_block(e, q2, 0)) + lane;
   __shared__ v4f red[kNW][2][64];
 
   for (int m0 = seg0; m0 < seg1; m0 += 16) {
@@ -142,19 +161,35 @@ __global__ __launch_bounds__(kNW * 64) void down_decode_kernel(
     const uint8_t* arow = hq + (size_t)(valid ? row : 0) * I + (lane >> 4) * 16;
     const uint8_t* srow = hs + (size_t)(valid ? row : 0) * (I / 32) + (lane >> 4);
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-    for (int j = j0; j < j1; ++j) {
-      v8i a = valid ? load_a_fp8(arow + (size_t)j * 128) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      const int sa = valid ? (int)srow[j * 4] : 127;
-      const uint8_t* wj = wblk + (size_t)j * 2048;
-      uint4 b[2];
+    for (int j = j0; j < j1; j += kBatch) {
+      uint4 b[kBatch][2];
+      uint32_t sw[kBatch];
+      v8i a[kBatch];
+      int sa[kBatch];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) b[t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
-      const uint32_t* sj = sblk + (size_t)(j >> 2) * 128;
-      const int sh = (j & 3) * 8;
+      for (int u = 0; u < kBatch; ++u) {
+        if (j + u < j1) {
+          const uint8_t* wj = wblk + (size_t)(j + u) * 2048;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int sb = (int)((sj[t * 64] >> sh) & 0xFFu);
-        acc[t] = mfma_fp8_fp4(a, widen_fp4(b[t]), acc[t], sa, sb);
+          for (int t = 0; t < 2; ++t) b[u][t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
+          sw[u] = sblk[(size_t)(j + u) * 64];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j + u < j1) {
+          a[u] = valid ? load_a_fp8(arow + (size_t)(j + u) * 128) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          sa[u] = valid ? (int)srow[(j + u) * 4] : 127;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j + u < j1) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[t] = mfma_fp8_fp4(a[u], widen_fp4(b[u][t]), acc[t], sa[u],
+                                  (int)((sw[u] >> (8 * t)) & 0xFFu));
+        }
       }
     }
 #pragma unroll

@@ -138,6 +138,7 @@ __global__ __launch_bounds__(256) void up_prefill_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (16 * (wm + 2 * i) < rows) nact = i + 1;
+  // weight scales: one dword per lane per K-step for each of the wave's 2 q-groups
   const uint32_t* sbp[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -148,7 +149,6 @@ __global__ __launch_bounds__(256) void up_prefill_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint32_t sbw[8];
 
   gload(0);
   lstore(0);
@@ -156,11 +156,9 @@ __global__ __launch_bounds__(256) void up_prefill_kernel(
   for (int j = 0; j < J; ++j) {
     const int buf = j & 1;
     if (j + 1 < J) gload(j + 1);
-    if ((j & 3) == 0) {
+    uint32_t sbq[2];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) sbw[t] = sbp[t >> 2][(size_t)(j >> 2) * 256 + (t & 3) * 64];
-    }
-    const int sh = (j & 3) * 8;
+    for (int qb = 0; qb < 2; ++qb) sbq[qb] = sbp[qb][(size_t)j * 64];
     v8i bf[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -174,7 +172,7 @@ __global__ __launch_bounds__(256) void up_prefill_kernel(
         const int sa = (int)((Ss[buf][row] >> (8 * (lane >> 4))) & 0xFFu);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          acc[i][t] = mfma_fp8_fp4(a, bf[t], acc[i][t], sa, (int)((sbw[t] >> sh) & 0xFFu));
+          acc[i][t] = mfma_fp8_fp4(a, bf[t], acc[i][t], sa, (int)((sbq[t >> 2] >> (8 * (t & 3))) & 0xFFu));
       }
     }
     if (j + 1 < J) lstore(buf ^ 1);
@@ -275,13 +273,13 @@ __global__ __launch_bounds__(256) void down_prefill_kernel(
   for (int i = 0; i < 4; ++i)
     if (16 * (wm + 2 * i) < rows) nact = i + 1;
   // this wave's weight tiles: q2-groups 8ft + 4wn + qb (qb 0..3), 2 tiles each: t = 2qb + tt
-  const uint32_t* sbp[4];
+  const uint16_t* sbp[4];
   bool gval[4];
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     const int g = 8 * ft + 4 * wn + qb;
     gval[qb] = g < QG;
-    sbp[qb] = reinterpret_cast<const uint32_t*>(packed + L.dns_block(e, gval[qb] ? g : 0, 0)) + lane;
+    sbp[qb] = reinterpret_cast<const uint16_t*>(packed + L.dns_block(e, gval[qb] ? g : 0, 0)) + lane;
   }
 
   v4f acc[4][8];
@@ -289,7 +287,6 @@ __global__ __launch_bounds__(256) void down_prefill_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint32_t sbw[8];
 
   gload(0);
   lstore(0);
@@ -297,11 +294,9 @@ __global__ __launch_bounds__(256) void down_prefill_kernel(
   for (int j = 0; j < J2; ++j) {
     const int buf = j & 1;
     if (j + 1 < J2) gload(j + 1);
-    if ((j & 3) == 0) {
+    uint32_t sbq[4];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) sbw[t] = sbp[t >> 1][(size_t)(j >> 2) * 128 + (t & 1) * 64];
-    }
-    const int sh = (j & 3) * 8;
+    for (int qb = 0; qb < 4; ++qb) sbq[qb] = sbp[qb][(size_t)j * 64];
     v8i bf[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -315,7 +310,7 @@ __global__ __launch_bounds__(256) void down_prefill_kernel(
         const int sa = (int)((Ss[buf][row] >> (8 * (lane >> 4))) & 0xFFu);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          acc[i][t] = mfma_fp8_fp4(a, bf[t], acc[i][t], sa, (int)((sbw[t] >> sh) & 0xFFu));
+          acc[i][t] = mfma_fp8_fp4(a, bf[t], acc[i][t], sa, (int)((sbq[t >> 1] >> (8 * (t & 1))) & 0xFFu));
       }
     }
     if (j + 1 < J2) lstore(buf ^ 1);

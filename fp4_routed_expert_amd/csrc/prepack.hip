@@ -32,23 +32,22 @@ __global__ void pack_up_weights(const uint4* __restrict__ w1, const uint4* __res
 __global__ void pack_up_scales(const uint8_t* __restrict__ s1, const uint8_t* __restrict__ s3,
                                PackedLayout L, uint32_t* __restrict__ out) {
   const int QT = L.I / 32;
-  const long n = (long)L.E * QT * L.JG * 256;
+  const long n = (long)L.E * QT * L.J * 64;  // one dword per (e, q, j, lane)
   for (long d = (long)blockIdx.x * blockDim.x + threadIdx.x; d < n;
        d += (long)gridDim.x * blockDim.x) {
-    const long blk = d >> 8;
-    const int t = (int)((d >> 6) & 3), l = (int)(d & 63);
-    const int jg = (int)(blk % L.JG);
-    const long eq = blk / L.JG;
+    const int l = (int)(d & 63);
+    const long blk = d >> 6;
+    const int j = (int)(blk % L.J);
+    const long eq = blk / L.J;
     const int q = (int)(eq % QT);
     const long e = eq / QT;
-    const long row = (long)q * 32 + (t & 1) * 16 + (l & 15);
-    const uint8_t* src = ((t < 2) ? s1 : s3) + (e * L.I + row) * (L.H / 32);
+    const long blkcol = (long)j * 4 + (l >> 4);  // 32-element block along H
     uint32_t v = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int js = 4 * jg + b;
-      const uint32_t code = (js < L.J) ? src[js * 4 + (l >> 4)] : 127u;
-      v |= code << (8 * b);
+    for (int t = 0; t < 4; ++t) {
+      const long row = (long)q * 32 + (t & 1) * 16 + (l & 15);
+      const uint8_t* src = (t < 2) ? s1 : s3;
+      v |= (uint32_t)src[(e * L.I + row) * (L.H / 32) + blkcol] << (8 * t);
     }
     out[(L.ups_off >> 2) + d] = v;
   }
@@ -73,27 +72,25 @@ __global__ void pack_down_weights(const uint4* __restrict__ w2, PackedLayout L,
 }
 
 __global__ void pack_down_scales(const uint8_t* __restrict__ s2, PackedLayout L,
-                                 uint32_t* __restrict__ out) {
+                                 uint16_t* __restrict__ out) {
   const int QT2 = L.H / 32;
-  const long n = (long)L.E * QT2 * L.JG2 * 128;
+  const long n = (long)L.E * QT2 * L.J2 * 64;  // one 16-bit pair per (e, q2, j2, lane)
   for (long d = (long)blockIdx.x * blockDim.x + threadIdx.x; d < n;
        d += (long)gridDim.x * blockDim.x) {
-    const long blk = d >> 7;
-    const int t = (int)((d >> 6) & 1), l = (int)(d & 63);
-    const int jg = (int)(blk % L.JG2);
-    const long eq = blk / L.JG2;
+    const int l = (int)(d & 63);
+    const long blk = d >> 6;
+    const int j2 = (int)(blk % L.J2);
+    const long eq = blk / L.J2;
     const int q2 = (int)(eq % QT2);
     const long e = eq / QT2;
-    const long row = (long)q2 * 32 + t * 16 + (l & 15);
-    const uint8_t* src = s2 + (e * L.H + row) * (L.I / 32);
+    const long blkcol = (long)j2 * 4 + (l >> 4);
     uint32_t v = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int js = 4 * jg + b;
-      const uint32_t code = (js < L.J2) ? src[js * 4 + (l >> 4)] : 127u;
-      v |= code << (8 * b);
+    for (int t = 0; t < 2; ++t) {
+      const long row = (long)q2 * 32 + t * 16 + (l & 15);
+      v |= (uint32_t)s2[(e * L.H + row) * (L.I / 32) + blkcol] << (8 * t);
     }
-    out[(L.dns_off >> 2) + d] = v;
+    out[(L.dns_off >> 1) + d] = (uint16_t)v;
   }
 }
 
@@ -111,12 +108,12 @@ hipError_t launch_prepack(const uint8_t* w1, const uint8_t* s1, const uint8_t* w
   hipLaunchKernelGGL(pack_up_weights, dim3(grid_for(L.E * QT * L.J * 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(w1), reinterpret_cast<const uint4*>(w3), L,
                      reinterpret_cast<uint4*>(packed));
-  hipLaunchKernelGGL(pack_up_scales, dim3(grid_for(L.E * QT * L.JG * 256)), dim3(256), 0, s, s1,
-                     s3, L, reinterpret_cast<uint32_t*>(packed));
+  hipLaunchKernelGGL(pack_up_scales, dim3(grid_for(L.E * QT * L.J * 64)), dim3(256), 0, s, s1, s3,
+                     L, reinterpret_cast<uint32_t*>(packed));
   hipLaunchKernelGGL(pack_down_weights, dim3(grid_for(L.E * QT2 * L.J2 * 128)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(w2), L, reinterpret_cast<uint4*>(packed));
-  hipLaunchKernelGGL(pack_down_scales, dim3(grid_for(L.E * QT2 * L.JG2 * 128)), dim3(256), 0, s,
-                     s2, L, reinterpret_cast<uint32_t*>(packed));
+  hipLaunchKernelGGL(pack_down_scales, dim3(grid_for(L.E * QT2 * L.J2 * 64)), dim3(256), 0, s, s2,
+                     L, reinterpret_cast<uint16_t*>(packed));
   return hipGetLastError();
 }
 

@@ -18,6 +18,10 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -52,7 +56,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
     best = wave_max_u64(best);
     const int e = E - 1 - (int)(uint32_t)best;
-    const float le = row[e];
+    const float le = from_ordered_bits((uint32_t)(best >> 32));  // the logit itself, no reload
     if (j == 0) l0 = le;
     if (lane == j) {
       my_id = e;

@@ -90,15 +90,20 @@ def _a256(x: int) -> int:
 
 
 def unpack_layout(packed: np.ndarray, E: int, H: int, I: int):
-    """Read the packed tile layout (as documented in the header of the kernels'
-    layout: 1 KiB MFMA B tiles, lane l = row l%16, K block l//16) back into
-    canonical w1, s1, w3, s3, w2, s2."""
+    """Read the packed tile layout back into canonical w1, s1, w3, s3, w2, s2.
+
+    Layout as documented with the kernels: 1 KiB MFMA B tiles (lane l holds
+    row l%16 and the 32 K elements of block l//16 as 16 bytes); gate/up blocks
+    of 4 tiles [W1 rows 0-15, W1 rows 16-31, W3 rows 0-15, W3 rows 16-31] per
+    (expert, 32-row group, K-step of 128), then per (expert, group, K-step) one
+    scale dword per lane (byte t = tile t); down blocks of 2 tiles and one
+    16-bit scale pair per lane."""
     J, J2 = H // 128, I // 128
-    JG, JG2 = (J + 3) // 4, (J2 + 3) // 4
     QT, QT2 = I // 32, H // 32
     upw = E * QT * J * 4096
-    ups = E * QT * JG * 1024
+    ups = E * QT * J * 256
     dnw = E * QT2 * J2 * 2048
+    dns = E * QT2 * J2 * 128
     o_ups = _a256(upw)
     o_dnw = _a256(o_ups + ups)
     o_dns = _a256(o_dnw + dnw)
@@ -106,16 +111,12 @@ def unpack_layout(packed: np.ndarray, E: int, H: int, I: int):
     w13 = a.transpose(0, 3, 1, 5, 2, 4, 6)                     # e t q lr j lg b
     w1 = w13[:, 0:2].transpose(0, 2, 1, 3, 4, 5, 6).reshape(E, I, H // 2)
     w3 = w13[:, 2:4].transpose(0, 2, 1, 3, 4, 5, 6).reshape(E, I, H // 2)
-    s = packed[o_ups:o_ups + ups].reshape(E, QT, JG, 4, 4, 16, 4)  # e q jg t lg lr b
-    s13 = s.transpose(0, 3, 1, 5, 2, 6, 4)                         # e t q lr jg b lg
-    s1 = s13[:, 0:2].transpose(0, 2, 1, 3, 4, 5, 6).reshape(E, I, JG * 16)
-    s3 = s13[:, 2:4].transpose(0, 2, 1, 3, 4, 5, 6).reshape(E, I, JG * 16)
-    pad13 = s1[:, :, H // 32:], s3[:, :, H // 32:]
+    s = packed[o_ups:o_ups + ups].reshape(E, QT, J, 4, 16, 4)   # e q j lg lr t
+    s13 = s.transpose(0, 5, 1, 4, 2, 3)                          # e t q lr j lg
+    s1 = s13[:, 0:2].transpose(0, 2, 1, 3, 4, 5).reshape(E, I, H // 32)
+    s3 = s13[:, 2:4].transpose(0, 2, 1, 3, 4, 5).reshape(E, I, H // 32)
     d = packed[o_dnw:o_dnw + dnw].reshape(E, QT2, J2, 2, 4, 16, 16)  # e q2 j2 t lg lr b
     w2 = d.transpose(0, 1, 3, 5, 2, 4, 6).reshape(E, H, I // 2)
-    ds = packed[o_dns:o_dns + E * QT2 * JG2 * 512].reshape(E, QT2, JG2, 2, 4, 16, 4)
-    s2 = ds.transpose(0, 1, 3, 5, 2, 6, 4).reshape(E, H, JG2 * 16)
-    pad2 = s2[:, :, I // 32:]
-    return (np.ascontiguousarray(w1), np.ascontiguousarray(s1[:, :, :H // 32]), np.ascontiguousarray(w3),
-            np.ascontiguousarray(s3[:, :, :H // 32]), np.ascontiguousarray(w2),
-            np.ascontiguousarray(s2[:, :, :I // 32]), pad13, pad2)
+    ds = packed[o_dns:o_dns + dns].reshape(E, QT2, J2, 4, 16, 2)     # e q2 j2 lg lr t
+    s2 = ds.transpose(0, 1, 5, 4, 2, 3).reshape(E, H, I // 32)
+    return tuple(np.ascontiguousarray(v) for v in (w1, s1, w3, s3, w2, s2))
