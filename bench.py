@@ -1,15 +1,18 @@
 """Benchmark of the FP4 routed-expert MoE layer on one MI355X.
 
 One step = the whole layer on one batch of synthetic inputs already resident
-in HBM: moe_route_topk -> moe_sort_permute -> moe_quant_act_mxfp8 ->
-moe_fp4_expert_up -> moe_fp4_expert_down -> moe_combine, all on one stream.
+in HBM, as one library call (moe_fp4_layer_forward: routing, sort/permute,
+MXFP8 of x, gate/up GEMM + SwiGLU, down GEMM, combine), on one stream.
 The default workload is the decode-shaped layer (T=8, H=4096, I=1536, E=64,
 top-6).  Several copies of the packed weights are cycled so that the 256 MB
 Infinity Cache cannot serve a step's weights from the previous step.
 
 Prints ONE JSON line (rank 0).  The dominant kernel (the gate/up expert GEMM)
-is timed with HIP events on the stream it runs on, and its algorithmic bytes
-per launch give the roofline fraction against 8 TB/s.  The CPU baseline is the
+is timed with HIP events on the stream it runs on, bracketing each of its
+launches in K further steps of the same layer run stage by stage through the
+single-stage calls right after the timed steps (same inputs, same weight
+copies); its algorithmic bytes (decode) or flops (prefill) per launch give
+the roofline fraction against 8 TB/s or the dense FP8 MFMA peak.  The CPU baseline is the
 oracle (a plain fp64 C implementation) on the host's cores, on a bounded
 sample of the same workload.
 """
@@ -162,35 +165,40 @@ def main():
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, k, E), 256),
                            dtype=torch.uint8, device=dev)
-    nsteps = args.warmup + args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 
-    def step(i, timed_idx=None):
+    lws = torch.empty(max(moe.layer_workspace_size(T, k, E, H, I, args.flags), 256),
+                      dtype=torch.uint8, device=dev)
+
+    def step(i):
+        moe.layer_forward(pws[i % copies], x, logits, k, args.flags, y=y, workspace=lws)
+
+    def staged_step(i, timed_idx):
         pw = pws[i % copies]
         moe.route_topk(logits, k, ids, gates)
         counts, offsets, sp, pp = moe.sort_permute(ids, E, out=sort_out, workspace=sort_ws)
         moe.quant_act_mxfp8(x, xq, xs)
-        if timed_idx is not None:
-            ev[timed_idx][0].record()
+        ev[timed_idx][0].record()
         moe.expert_up(pw, xq, xs, offsets, sp, T, k, args.flags, hq=hq, hs=hs, workspace=stage_ws)
-        if timed_idx is not None:
-            ev[timed_idx][1].record()
+        ev[timed_idx][1].record()
         moe.expert_down(pw, hq, hs, offsets, T, k, args.flags, O=O, workspace=stage_ws)
         moe.combine(O, gates, pp, T, k, H, y=y)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    counts = sort_out[0].cpu().numpy()
-    used = int((counts > 0).sum())
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, i)
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dt = t1 - t0
+    for i in range(args.steps):
+        staged_step(args.warmup + i, i)
+    torch.cuda.synchronize()
     up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    counts = sort_out[0].cpu().numpy()
+    used = int((counts > 0).sum())
 
     ms_per_step = dt / args.steps * 1e3
     tokens_per_s = T * args.steps / dt

@@ -22,7 +22,7 @@ from ._lib import (MOE_FLAG_FORCE_DECODE, MOE_FLAG_FORCE_PREFILL, MoeError,  # n
 __all__ = [
     "route_topk", "sort_permute", "quant_act_mxfp8", "prepack_weights", "PackedWeights",
     "expert_up", "expert_down", "combine", "grouped_forward", "moe_layer",
-    "forward_workspace_size", "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
+    "forward_workspace_size", "layer_forward", "layer_workspace_size", "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
 ]
 
 
@@ -197,6 +197,31 @@ def grouped_forward(pw: PackedWeights, xq, xs, gates, offsets, sorted_pair, pair
         ctypes.byref(pw.desc), _ptr(xq), _ptr(xs), _ptr(gates), _ptr(offsets), _ptr(sorted_pair),
         _ptr(pair_pos), T, k, _ptr(y), _ptr(workspace), workspace.numel(), flags, _stream(xq)),
         "moe_fp4_grouped_forward")
+    return y
+
+
+def layer_workspace_size(T: int, k: int, E: int, H: int, I: int, flags: int = 0) -> int:
+    return int(_lib.lib().moe_fp4_layer_workspace_size(T, k, E, H, I, flags))
+
+
+def layer_forward(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: int, flags: int = 0,
+                  y=None, workspace=None):
+    """The whole layer in one library call (moe_fp4_layer_forward) -> y [T, H] fp32."""
+    _check_dtype(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
+    _check_dtype(logits, (torch.float32,), "logits")
+    T, H = x.shape
+    if logits.shape[0] != T or H != pw.H or logits.shape[1] != pw.E:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, logits {tuple(logits.shape)}, "
+                         f"weights E={pw.E} H={pw.H}")
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = layer_workspace_size(T, k, pw.E, pw.H, pw.I, flags)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _lib.check(_lib.lib().moe_fp4_layer_forward(
+        ctypes.byref(pw.desc), _ptr(x), _ptr(logits), T, k, _ptr(y), _ptr(workspace),
+        workspace.numel(), flags, _stream(x)), "moe_fp4_layer_forward")
     return y
 
 

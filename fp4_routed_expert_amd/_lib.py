@@ -65,6 +65,8 @@ SIGNATURES = {
     "moe_fp4_forward_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _U32]),
     "moe_fp4_grouped_forward": (ctypes.c_int, [_WP, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _SZ,
                                                _U32, _P]),
+    "moe_fp4_layer_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _U32]),
+    "moe_fp4_layer_forward": (ctypes.c_int, [_WP, _P, _P, _I32, _I32, _P, _P, _SZ, _U32, _P]),
 }
 
 

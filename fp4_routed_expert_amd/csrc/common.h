@@ -142,6 +142,12 @@ struct PackedLayout {
 
 // ------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch(es).
+constexpr int kFrontMaxT = 32;  // token counts taken by the fused front kernel
+int route_keys_per_lane(int E);
+hipError_t launch_front_small(const float* logits, const uint16_t* x, int T, int H, int E, int k,
+                              int32_t* ids, float* gates, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, uint8_t* xq, uint8_t* xs,
+                              hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids,
                              float* gates, hipStream_t s);
 size_t sort_workspace_bytes(int T, int E, int k);

@@ -2,46 +2,52 @@
 //
 // With a handful of tokens per expert the layer is bound by reading the packed
 // FP4 weights from HBM once.  One workgroup owns one expert and 32 output rows
-// and streams those rows' packed tiles over the whole K range, its four waves
+// and streams those rows' packed tiles over the whole K range, its waves
 // splitting K; each wave issues 128-bit loads of whole 1 KiB tiles (a tile is
 // contiguous in the packed layout, so a wave's load is one 1 KiB run) plus one
-// dword per lane per K-step holding the four tiles' E8M0 scales.  Each wave
-// issues the loads of kBatch K-steps back to back before using them, so that
-// enough bytes are in flight per CU to cover HBM latency.  The dot products run on
-// the gfx950 scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, MXFP8 activations
-// as A, FP4 weights as B, one E8M0 scale per lane and operand), which applies
-// the block scales in hardware: the token rows are padded to 16, compute is far
-// below the roofline here.  The four waves' partial sums are added in a fixed
-// order through LDS (no atomics: pwwt.cn review, section 4.2), then wave 0
-// runs the epilogue -- SwiGLU and MXFP8 requantisation of h for the gate/up
-// kernel, the fp32 store of O for the down kernel.
+// word per lane per K-step holding the tiles' E8M0 scales.  A wave's K-steps
+// are taken in batches of kB whose loads are issued back to back; with
+// pipelining on, the loads of the next batch are in flight while the current
+// one is multiplied, so each wave keeps one to two batches of weight bytes
+// outstanding all the time.  The dot products run on the gfx950 scaled MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4, MXFP8 activations as A, FP4 weights as
+// B, one E8M0 scale per lane and operand), which applies the block scales in
+// hardware: the token rows are padded to 16, compute is far below the
+// roofline here.  The waves' partial sums are added in a fixed order through
+// LDS (no atomics: pwwt.cn review, section 4.2), then wave 0 runs the epilogue
+// -- SwiGLU and MXFP8 requantisation of h for the gate/up kernel, the fp32
+// store of O for the down kernel.
 #include "common.h"
+
+#ifndef DEC_UP_NW
+#define DEC_UP_NW 4
+#endif
+#ifndef DEC_UP_B
+#define DEC_UP_B 4
+#endif
+#ifndef DEC_UP_PIPE
+#define DEC_UP_PIPE 0
+#endif
+#ifndef DEC_DN_NW
+#define DEC_DN_NW 4
+#endif
+#ifndef DEC_DN_B
+#define DEC_DN_B 4
+#endif
+#ifndef DEC_DN_PIPE
+#define DEC_DN_PIPE 0
+#endif
 
 namespace moe {
 namespace {
 
-constexpr int kNW = 4;     // waves per workgroup, splitting K
-constexpr int kBatch = 4;  // K-steps whose loads a wave issues together
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-// A operand (fp8) of the 16x16x128 scaled MFMA: lane l holds row l%16 and, for
-// g = l/16, K elements [16g, 16g+16) in bytes 0-15 and [64+16g, 64+16g+16) in
-// bytes 16-31 (measured on gfx950 with single-hot operands).  The A scale of
-// (row m, 32-block b) is taken from lane 16b + m, i.e. lane l supplies the
-// scale of block l/16 of its row.  `p` points at row + 16*(l/16).
-__device__ __forceinline__ v8i load_a_fp8(const uint8_t* p) {
-  const uint4 a0 = *reinterpret_cast<const uint4*>(p);
-  const uint4 a1 = *reinterpret_cast<const uint4*>(p + 64);
-  v8i r;
-  r[0] = (int)a0.x; r[1] = (int)a0.y; r[2] = (int)a0.z; r[3] = (int)a0.w;
-  r[4] = (int)a1.x; r[5] = (int)a1.y; r[6] = (int)a1.z; r[7] = (int)a1.w;
-  return r;
-}
-
+// The FP4 B operand occupies four registers; the builtin's operand is eight
+// wide, the upper half is never read for the e2m1 format.
 __device__ __forceinline__ v8i widen_fp4(uint4 b) {
-  v8i r;
-  r[0] = (int)b.x; r[1] = (int)b.y; r[2] = (int)b.z; r[3] = (int)b.w;
-  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
-  return r;
+  const v4i v = v4i{(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
 __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c, int sa, int sb) {
@@ -49,7 +55,101 @@ __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c, int sa, int sb)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
 }
 
-__global__ __launch_bounds__(kNW * 64) void up_decode_kernel(
+// Registers of one K-step: NT weight tiles and their scale word, plus the A
+// fragment.  A operand (fp8) of the 16x16x128 scaled MFMA: lane l holds row
+// l%16 and, for g = l/16, K elements [16g, 16g+16) in a0 and [64+16g,
+// 64+16g+16) in a1 (measured on gfx950 with single-hot operands).  The A
+// scale of (row m, 32-block b) is taken from lane 16b + m, i.e. lane l
+// supplies the scale of block l/16 of its row.
+template <int NT>
+struct Step {
+  uint4 b[NT];
+  uint32_t sw;
+  uint4 a0, a1;
+  uint32_t sa;
+};
+
+// Per-wave streaming state: where the wave's tiles, scales and A rows start.
+template <int NT>
+struct Stream {
+  const uint8_t* w;   // packed tiles of K-step 0, this lane's 16 bytes
+  const uint8_t* s;   // scale words of K-step 0, this lane's word
+  const uint8_t* a;   // activation row of this lane at K-step 0 (+16 * (lane / 16))
+  const uint8_t* as;  // activation scale of this lane at K-step 0 (+lane / 16)
+  bool valid;         // the lane's row is a real pair
+};
+
+template <int NT>
+__device__ __forceinline__ void load_step(Step<NT>& r, const Stream<NT>& st, int j) {
+  const uint8_t* wj = st.w + (size_t)j * (NT * 1024);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) r.b[t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
+  if constexpr (NT == 4)
+    r.sw = *reinterpret_cast<const uint32_t*>(st.s + (size_t)j * 256);
+  else
+    r.sw = *reinterpret_cast<const uint16_t*>(st.s + (size_t)j * 128);
+  if (st.valid) {
+    r.a0 = *reinterpret_cast<const uint4*>(st.a + (size_t)j * 128);
+    r.a1 = *reinterpret_cast<const uint4*>(st.a + (size_t)j * 128 + 64);
+    r.sa = st.as[j * 4];
+  } else {
+    r.a0 = make_uint4(0, 0, 0, 0);
+    r.a1 = make_uint4(0, 0, 0, 0);
+    r.sa = 127;
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void mma_step(const Step<NT>& r, v4f* acc) {
+  v8i a;
+  a[0] = (int)r.a0.x; a[1] = (int)r.a0.y; a[2] = (int)r.a0.z; a[3] = (int)r.a0.w;
+  a[4] = (int)r.a1.x; a[5] = (int)r.a1.y; a[6] = (int)r.a1.z; a[7] = (int)r.a1.w;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    acc[t] = mfma_fp8_fp4(a, widen_fp4(r.b[t]), acc[t], (int)r.sa, (int)((r.sw >> (8 * t)) & 0xFFu));
+}
+
+template <int NT, int kB>
+__device__ __forceinline__ void load_batch(Step<NT> (&r)[kB], const Stream<NT>& st, int j, int j1) {
+#pragma unroll
+  for (int u = 0; u < kB; ++u)
+    if (j + u < j1) load_step<NT>(r[u], st, j + u);
+}
+
+template <int NT, int kB>
+__device__ __forceinline__ void mma_batch(const Step<NT> (&r)[kB], v4f* acc, int j, int j1) {
+#pragma unroll
+  for (int u = 0; u < kB; ++u)
+    if (j + u < j1) mma_step<NT>(r[u], acc);
+}
+
+// Multiply-accumulate K-steps [j0, j1) of one wave into acc.
+template <int NT, int kB, bool kPipe>
+__device__ __forceinline__ void stream_k(const Stream<NT>& st, int j0, int j1, v4f* acc) {
+  if constexpr (!kPipe) {
+    for (int j = j0; j < j1; j += kB) {
+      Step<NT> r[kB];
+      load_batch<NT, kB>(r, st, j, j1);
+      mma_batch<NT, kB>(r, acc, j, j1);
+    }
+  } else {
+    // two register sets taken in turn, so no loaded register is ever copied
+    Step<NT> x[kB], y[kB];
+    if (j0 < j1) load_batch<NT, kB>(x, st, j0, j1);
+    for (int j = j0; j < j1; j += 2 * kB) {
+      if (j + kB < j1) load_batch<NT, kB>(y, st, j + kB, j1);
+      mma_batch<NT, kB>(x, acc, j, j1);
+      if (j + kB >= j1) break;
+      if (j + 2 * kB < j1) load_batch<NT, kB>(x, st, j + 2 * kB, j1);
+      mma_batch<NT, kB>(y, acc, j + kB, j1);
+    }
+  }
+}
+
+constexpr int kUpNW = DEC_UP_NW;
+constexpr int kDnNW = DEC_DN_NW;
+
+__global__ __launch_bounds__(kUpNW * 64) void up_decode_kernel(
     const uint8_t* __restrict__ packed, PackedLayout L, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xs, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, int k, uint8_t* __restrict__ hq,
@@ -60,51 +160,22 @@ __global__ __launch_bounds__(kNW * 64) void up_decode_kernel(
   if (seg0 >= seg1) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = L.H, I = L.I, J = L.J;
-  const int j0 = (wave * J) / kNW, j1 = ((wave + 1) * J) / kNW;
-  const uint8_t* wblk = packed + L.upw_block(e, q, 0) + lane * 16;
-  const uint32_t* sblk = reinterpret_cast<const uint32_t*>(packed + L.ups_block(e, q, 0)) + lane;
-  __shared__ v4f red[kNW][4][64];
+  const int j0 = (wave * J) / kUpNW, j1 = ((wave + 1) * J) / kUpNW;
+  __shared__ v4f red[kUpNW][4][64];
 
   for (int m0 = seg0; m0 < seg1; m0 += 16) {
     const int row = m0 + (lane & 15);
-    const bool valid = row < seg1;
-    const int tok = valid ? sorted_pair[row] / k : 0;
-    const uint8_t* arow = xq + (size_t)tok * H + (lane >> 4) * 16;
-    const uint8_t* srow = xs + (size_t)tok * (H / 32) + (lane >> 4);
+    Stream<4> st;
+    st.valid = row < seg1;
+    const int tok = st.valid ? sorted_pair[row] / k : 0;
+    st.w = packed + L.upw_block(e, q, 0) + lane * 16;
+    st.s = packed + L.ups_block(e, q, 0) + lane * 4;
+    st.a = xq + (size_t)tok * H + (lane >> 4) * 16;
+    st.as = xs + (size_t)tok * (H / 32) + (lane >> 4);
     v4f acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int j = j0; j < j1; j += kBatch) {
-      uint4 b[kBatch][4];
-      uint32_t sw[kBatch];
-      v8i a[kBatch];
-      int sa[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j + u < j1) {
-          const uint8_t* wj = wblk + (size_t)(j + u) * 4096;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) b[u][t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
-          sw[u] = sblk[(size_t)(j + u) * 64];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j + u < j1) {
-          a[u] = valid ? load_a_fp8(arow + (size_t)(j + u) * 128) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          sa[u] = valid ? (int)srow[(j + u) * 4] : 127;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j + u < j1) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[t] = mfma_fp8_fp4(a[u], widen_fp4(b[u][t]), acc[t], sa[u],
-                                  (int)((sw[u] >> (8 * t)) & 0xFFu));
-        }
-      }
-    }
+    stream_k<4, DEC_UP_B, DEC_UP_PIPE != 0>(st, j0, j1, acc);
 #pragma unroll
     for (int t = 0; t < 4; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
@@ -114,7 +185,7 @@ __global__ __launch_bounds__(kNW * 64) void up_decode_kernel(
       for (int t = 0; t < 4; ++t) {
         s[t] = red[0][t][lane];
 #pragma unroll
-        for (int w = 1; w < kNW; ++w) s[t] += red[w][t][lane];
+        for (int w = 1; w < kUpNW; ++w) s[t] += red[w][t][lane];
       }
       // lane holds rows 4*(lane>>4)+v of the tile, column lane&15 of each
       // 16-row group: tiles 0/1 are G for i = 32q + c and 32q + 16 + c,
@@ -141,7 +212,7 @@ __global__ __launch_bounds__(kNW * 64) void up_decode_kernel(
   }
 }
 
-__global__ __launch_bounds__(kNW * 64) void down_decode_kernel(
+__global__ __launch_bounds__(kDnNW * 64) void down_decode_kernel(
     const uint8_t* __restrict__ packed, PackedLayout L, const uint8_t* __restrict__ hq,
     const uint8_t* __restrict__ hs, const int32_t* __restrict__ offsets, float* __restrict__ O) {
   const int QT2 = L.H / 32;
@@ -150,48 +221,20 @@ __global__ __launch_bounds__(kNW * 64) void down_decode_kernel(
   if (seg0 >= seg1) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = L.H, I = L.I, J2 = L.J2;
-  const int j0 = (wave * J2) / kNW, j1 = ((wave + 1) * J2) / kNW;
-  const uint8_t* wblk = packed + L.dnw_block(e, q2, 0) + lane * 16;
-  const uint16_t* sblk = reinterpret_cast<const uint16_t*>(packed + L.dns_block(e, q2, 0)) + lane;
-  __shared__ v4f red[kNW][2][64];
+  const int j0 = (wave * J2) / kDnNW, j1 = ((wave + 1) * J2) / kDnNW;
+  __shared__ v4f red[kDnNW][2][64];
 
   for (int m0 = seg0; m0 < seg1; m0 += 16) {
     const int row = m0 + (lane & 15);
-    const bool valid = row < seg1;
-    const uint8_t* arow = hq + (size_t)(valid ? row : 0) * I + (lane >> 4) * 16;
-    const uint8_t* srow = hs + (size_t)(valid ? row : 0) * (I / 32) + (lane >> 4);
+    Stream<2> st;
+    st.valid = row < seg1;
+    const int rr = st.valid ? row : 0;
+    st.w = packed + L.dnw_block(e, q2, 0) + lane * 16;
+    st.s = packed + L.dns_block(e, q2, 0) + lane * 2;
+    st.a = hq + (size_t)rr * I + (lane >> 4) * 16;
+    st.as = hs + (size_t)rr * (I / 32) + (lane >> 4);
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-    for (int j = j0; j < j1; j += kBatch) {
-      uint4 b[kBatch][2];
-      uint32_t sw[kBatch];
-      v8i a[kBatch];
-      int sa[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j + u < j1) {
-          const uint8_t* wj = wblk + (size_t)(j + u) * 2048;
-#pragma unroll
-          for (int t = 0; t < 2; ++t) b[u][t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
-          sw[u] = sblk[(size_t)(j + u) * 64];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j + u < j1) {
-          a[u] = valid ? load_a_fp8(arow + (size_t)(j + u) * 128) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          sa[u] = valid ? (int)srow[(j + u) * 4] : 127;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j + u < j1) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[t] = mfma_fp8_fp4(a[u], widen_fp4(b[u][t]), acc[t], sa[u],
-                                  (int)((sw[u] >> (8 * t)) & 0xFFu));
-        }
-      }
-    }
+    stream_k<2, DEC_DN_B, DEC_DN_PIPE != 0>(st, j0, j1, acc);
 #pragma unroll
     for (int t = 0; t < 2; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
@@ -200,7 +243,7 @@ __global__ __launch_bounds__(kNW * 64) void down_decode_kernel(
       for (int t = 0; t < 2; ++t) {
         v4f s = red[0][t][lane];
 #pragma unroll
-        for (int w = 1; w < kNW; ++w) s += red[w][t][lane];
+        for (int w = 1; w < kDnNW; ++w) s += red[w][t][lane];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = m0 + 4 * (lane >> 4) + v;
@@ -219,7 +262,7 @@ hipError_t launch_up_decode(const uint8_t* packed, const PackedLayout& L, const 
                             const int32_t* sorted_pair, int k, uint8_t* hq, uint8_t* hs,
                             hipStream_t s) {
   const unsigned grid = (unsigned)L.E * (unsigned)(L.I / 32);
-  hipLaunchKernelGGL(up_decode_kernel, dim3(grid), dim3(kNW * 64), 0, s, packed, L, xq, xs,
+  hipLaunchKernelGGL(up_decode_kernel, dim3(grid), dim3(kUpNW * 64), 0, s, packed, L, xq, xs,
                      offsets, sorted_pair, k, hq, hs);
   return hipGetLastError();
 }
@@ -228,7 +271,7 @@ hipError_t launch_down_decode(const uint8_t* packed, const PackedLayout& L, cons
                               const uint8_t* hs, const int32_t* offsets, float* O,
                               hipStream_t s) {
   const unsigned grid = (unsigned)L.E * (unsigned)(L.H / 32);
-  hipLaunchKernelGGL(down_decode_kernel, dim3(grid), dim3(kNW * 64), 0, s, packed, L, hq, hs,
+  hipLaunchKernelGGL(down_decode_kernel, dim3(grid), dim3(kDnNW * 64), 0, s, packed, L, hq, hs,
                      offsets, O);
   return hipGetLastError();
 }

@@ -1,0 +1,87 @@
+// Fused front of the layer for small token counts: top-k routing, the stable
+// expert sort and the MXFP8 quantisation of x in one launch.
+//
+// For a decode batch each front stage is a few microseconds of pure latency,
+// so they share one grid: block 0 routes every token (one wave per token, the
+// next token's logits loaded while the current one is ranked), keeps the
+// expert ids in LDS and sorts them there (the same histogram / scan / stable
+// scatter as the stand-alone sort); blocks 1.. quantise x, 2048 elements each,
+// while block 0 works.  Outputs are identical to the three stand-alone
+// kernels'.
+#include "stages.h"
+
+namespace moe {
+namespace {
+
+constexpr int kFrontThreads = 256;
+constexpr int kFrontWaves = kFrontThreads / 64;
+constexpr int kFrontMaxP = kFrontMaxT * 32;  // k <= 32
+
+template <int NK>
+__global__ __launch_bounds__(kFrontThreads) void front_small_kernel(
+    const float* __restrict__ logits, const uint4* __restrict__ x, int T, int E, int k, long n8,
+    int32_t* __restrict__ ids, float* __restrict__ gates, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_pos, uint2* __restrict__ xq, uint8_t* __restrict__ xs) {
+  if (blockIdx.x > 0) {
+    quant_group8(x, (long)(blockIdx.x - 1) * kFrontThreads + threadIdx.x, n8, xq, xs);
+    return;
+  }
+  __shared__ SortSmallLds sm;
+  __shared__ int sids[kFrontMaxP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float raw[NK];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = lane + 64 * i;
+      raw[i] = (e < E) ? logits[(size_t)t * E + e] : 0.0f;
+    }
+  };
+  if (wave < T) fetch(wave);
+  for (int t = wave; t < T; t += kFrontWaves) {
+    RouteKeys<NK> r;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = lane + 64 * i;
+      r.key[i] = (e < E) ? (((uint64_t)ordered_bits(raw[i]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+    }
+    if (t + kFrontWaves < T) fetch(t + kFrontWaves);
+    int id;
+    float g;
+    if (route_topk_token<NK>(r, E, k, lane, &id, &g)) {
+      ids[(size_t)t * k + lane] = id;
+      gates[(size_t)t * k + lane] = g;
+      sids[t * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  sort_small_body(sids, T * k, E, sm, counts, offsets, sorted_pair, pair_pos);
+}
+
+}  // namespace
+
+hipError_t launch_front_small(const float* logits, const uint16_t* x, int T, int H, int E, int k,
+                              int32_t* ids, float* gates, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, uint8_t* xq, uint8_t* xs,
+                              hipStream_t s) {
+  if (T < 1 || T > kFrontMaxT || k > 32) return hipErrorInvalidValue;
+  const long n8 = (long)T * H / 8;
+  const dim3 grid((unsigned)(1 + (n8 + kFrontThreads - 1) / kFrontThreads)), block(kFrontThreads);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint2* qv = reinterpret_cast<uint2*>(xq);
+#define MOE_FRONT(nk)                                                                             \
+  hipLaunchKernelGGL(front_small_kernel<nk>, grid, block, 0, s, logits, xv, T, E, k, n8, ids,     \
+                     gates, counts, offsets, sorted_pair, pair_pos, qv, xs)
+  switch (route_keys_per_lane(E)) {
+    case 1: MOE_FRONT(1); break;
+    case 2: MOE_FRONT(2); break;
+    case 4: MOE_FRONT(4); break;
+    case 8: MOE_FRONT(8); break;
+    default: MOE_FRONT(16); break;
+  }
+#undef MOE_FRONT
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -79,6 +79,28 @@ FwdCarve carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
   return c;
 }
 
+struct LayerCarve {
+  size_t ids, gates, counts, offsets, sorted, pos, sort_ws, xq, xs, fwd, fwd_bytes, total;
+};
+
+LayerCarve layer_carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+  const size_t P = (size_t)T * (size_t)k;
+  LayerCarve c;
+  c.ids = 0;
+  c.gates = align256(c.ids + P * 4);
+  c.counts = align256(c.gates + P * 4);
+  c.offsets = align256(c.counts + (size_t)E * 4);
+  c.sorted = align256(c.offsets + ((size_t)E + 1) * 4);
+  c.pos = align256(c.sorted + P * 4);
+  c.sort_ws = align256(c.pos + P * 4);
+  c.xq = align256(c.sort_ws + sort_workspace_bytes(T, E, k));
+  c.xs = align256(c.xq + (size_t)T * H);
+  c.fwd = align256(c.xs + (size_t)T * (H / 32));
+  c.fwd_bytes = carve(T, k, E, H, I).total;
+  c.total = align256(c.fwd + c.fwd_bytes);
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,6 +289,58 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w, const uint8_t* 
   st = moe_fp4_expert_down(w, hq, hs, expert_offsets, T, k, O, stage, stage_bytes, flags, stream);
   if (st != MOE_OK) return st;
   return moe_combine(O, topk_gates, pair_pos, T, k, w->H, y, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t moe_fp4_layer_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                    uint32_t flags) {
+  (void)flags;
+  if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
+  return layer_carve(T, k, E, H, I).total;
+}
+
+moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w, const uint16_t* x_bf16,
+                                   const float* logits, int32_t T, int32_t k, float* y,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   hipStream_t stream) {
+  moe_status_t st = check_weights(w);
+  if (st != MOE_OK) return st;
+  st = check_tek(T, w->E, k);
+  if (st != MOE_OK) return st;
+  if (select_path((int64_t)T * k, w->E, flags) < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !logits || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_bf16, 16) || !aligned(logits, 4) || !aligned(y, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t E = w->E, H = w->H, I = w->I;
+  const LayerCarve c = layer_carve(T, k, E, H, I);
+  if (!workspace || workspace_bytes < c.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
+  float* gates = reinterpret_cast<float*>(ws + c.gates);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + c.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + c.sorted);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + c.pos);
+  uint8_t* xq = ws + c.xq;
+  uint8_t* xs = ws + c.xs;
+  if (T <= kFrontMaxT) {
+    st = hip_status(launch_front_small(logits, x_bf16, T, H, E, k, ids, gates, counts, offsets,
+                                       sorted, pos, xq, xs, stream));
+  } else {
+    st = hip_status(launch_route_topk(logits, T, E, k, ids, gates, stream));
+    if (st == MOE_OK)
+      st = hip_status(launch_sort_permute(ids, T, E, k, counts, offsets, sorted, pos,
+                                          ws + c.sort_ws, stream));
+    if (st == MOE_OK) st = hip_status(launch_quant_mxfp8(x_bf16, T, H, xq, xs, stream));
+  }
+  if (st != MOE_OK) return st;
+  return moe_fp4_grouped_forward(w, xq, xs, gates, offsets, sorted, pos, T, k, y, ws + c.fwd,
+                                 c.fwd_bytes, flags, stream);
 }
 
 }  // extern "C"

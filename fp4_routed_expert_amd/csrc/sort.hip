@@ -10,7 +10,7 @@
 // P <= kChunk pairs: one workgroup does histogram, scan and scatter.
 // Larger P: (1) per-chunk histograms, (2) one workgroup scans them in
 // (expert, chunk) order, (3) each chunk scatters from its own base.
-#include "common.h"
+#include "stages.h"
 
 namespace moe {
 namespace {
@@ -18,67 +18,13 @@ namespace {
 constexpr int kThreads = 256;           // 4 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 4096;            // pairs per workgroup
-constexpr int kMaxE = 1024;
-
-// Stable scatter of pairs [p0, p1) given base[e] = first free sorted position
-// of expert e for this range.  table is [kWaves][E] of zeros on entry and exit.
-__device__ void stable_scatter(const int32_t* __restrict__ ids, int p0, int p1, int E, int* base,
-                               int* table, int32_t* __restrict__ sorted_pair,
-                               int32_t* __restrict__ pair_pos) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c = p0; c < p1; c += kThreads) {
-    const int p = c + tid;
-    const bool valid = p < p1;
-    const int id = valid ? ids[p] : kMaxE;  // sentinel outside [0, E)
-    // lanes holding the same id: intersect the 11 bit-planes of the ids
-    uint64_t same = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 11; ++b) {
-      const uint64_t ones = __ballot((id >> b) & 1);
-      same &= ((id >> b) & 1) ? ones : ~ones;
-    }
-    const int rank = __popcll(same & lt_mask);
-    const int cnt = __popcll(same);
-    const bool leader = valid && rank == 0;
-    if (leader) table[w * E + id] = cnt;
-    __syncthreads();
-    if (valid) {
-      int pre = 0;
-      for (int i = 0; i < w; ++i) pre += table[i * E + id];
-      const int pos = base[id] + pre + rank;
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
-    }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&base[id], cnt);  // integer: order-free
-      table[w * E + id] = 0;
-    }
-    __syncthreads();
-  }
-}
 
 __global__ __launch_bounds__(kThreads) void sort_small_kernel(
     const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_pos) {
-  __shared__ int hist[kMaxE];
-  __shared__ int table[kWaves * kMaxE];
-  __shared__ int wave_tot[kWaves];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kThreads) hist[e] = 0;
-  for (int i = tid; i < kWaves * E; i += kThreads) table[i] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += kThreads) atomicAdd(&hist[ids[p]], 1);
-  __syncthreads();
-  for (int e = tid; e < E; e += kThreads) counts[e] = hist[e];
-  __syncthreads();
-  const int total = block_exclusive_scan256(hist, E, wave_tot);
-  for (int e = tid; e < E; e += kThreads) offsets[e] = hist[e];
-  if (tid == 0) offsets[E] = total;
-  __syncthreads();
-  stable_scatter(ids, 0, P, E, hist, table, sorted_pair, pair_pos);
+  __shared__ SortSmallLds sm;
+  sort_small_body(ids, P, E, sm, counts, offsets, sorted_pair, pair_pos);
 }
 
 __global__ __launch_bounds__(kThreads) void sort_hist_kernel(const int32_t* __restrict__ ids,
@@ -131,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void sort_scatter_kernel(
   for (int i = tid; i < kWaves * E; i += kThreads) table[i] = 0;
   __syncthreads();
   const int p0 = blockIdx.x * kChunk, p1 = min(P, p0 + kChunk);
-  stable_scatter(ids, p0, p1, E, base, table, sorted_pair, pair_pos);
+  stable_scatter<kThreads>(ids, p0, p1, E, base, table, sorted_pair, pair_pos);
 }
 
 }  // namespace

@@ -203,6 +203,27 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w /*(host)*/,
                                      float* y, void* workspace, size_t workspace_bytes,
                                      uint32_t flags, hipStream_t stream);
 
+/*
+ * The whole layer, steps 1-7, in one call: route -> sort/permute -> MXFP8(x)
+ * -> expert_up -> expert_down -> combine.  Results are bitwise identical to
+ * the chain of the single-stage calls above on the same inputs.  For
+ * T <= 32 the three front steps run as one fused launch (routing and sort in
+ * one workgroup, quantisation in the others); larger T uses the stand-alone
+ * kernels.  Every intermediate lives in `workspace`
+ * (>= moe_fp4_layer_workspace_size(T, k, E, H, I, flags) bytes, 256-aligned;
+ * contents on entry are ignored, on exit unspecified).
+ *   x_bf16 [T, H] bf16 bits (16-byte aligned); logits [T, E] fp32
+ *   y [T, H] fp32 (out, overwritten, 16-byte aligned)
+ *   flags: MOE_FLAG_FORCE_DECODE / MOE_FLAG_FORCE_PREFILL as above
+ */
+size_t moe_fp4_layer_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                    uint32_t flags);
+moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w /*(host)*/,
+                                   const uint16_t* x_bf16, const float* logits,
+                                   int32_t T, int32_t k, float* y,
+                                   void* workspace, size_t workspace_bytes,
+                                   uint32_t flags, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     so = ctypes.CDLL(_lib.SO_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -117,6 +117,24 @@ def test_forward_argument_errors():
     assert up(ctypes.byref(d), A, A, A, A, 16, 2, A, A, A, sws - 1, 0, NUL) == WSE
     assert L.moe_combine(A, A, A, 4, 2, 250, A, NUL) == UNS       # H % 4
     assert L.moe_combine(A, A, A, 4, 0, 256, A, NUL) == INV
+
+
+def test_layer_forward_argument_errors():
+    d = _desc()
+    need = L.moe_fp4_layer_workspace_size(16, 2, 8, 256, 128, 0)
+    # holds at least the forward workspace plus ids, gates, sort arrays and MXFP8 x
+    assert need >= L.moe_fp4_forward_workspace_size(16, 2, 8, 256, 128, 0) + 16 * 256
+    assert L.moe_fp4_layer_workspace_size(16, 9, 8, 256, 128, 0) == 0   # k > E
+    lf = L.moe_fp4_layer_forward
+    assert lf(ctypes.byref(d), A, A, 16, 2, A, A, need - 1, 0, NUL) == WSE
+    assert lf(ctypes.byref(d), A, A, 16, 2, A, NUL, need, 0, NUL) == WSE
+    assert lf(ctypes.byref(d), A, A, 16, 2, A, MIS, need, 0, NUL) == INV
+    assert lf(ctypes.byref(d), MIS, A, 16, 2, A, A, need, 0, NUL) == INV   # x not 16-aligned
+    assert lf(ctypes.byref(d), A, NUL, 16, 2, A, A, need, 0, NUL) == INV
+    assert lf(ctypes.byref(d), A, A, 16, 2, A, A, need, 3, NUL) == INV     # both paths forced
+    assert lf(ctypes.byref(d), A, A, 16, 40, A, A, need, 0, NUL) == UNS    # k > 32
+    assert lf(ctypes.byref(_desc(version=2)), A, A, 16, 2, A, A, need, 0, NUL) == INV
+    assert lf(ctypes.byref(d), NUL, NUL, 0, 2, NUL, NUL, 0, 0, NUL) == 0  # T = 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
