@@ -13,8 +13,8 @@
 // and no count is ever read back to the host; workgroups past the tile count
 // exit.  kBM = 192 covers a whole expert at the prefill shape (113-180 rows
 // per expert), so each expert's packed weights stream from HBM once per
-// feature tile; 16-row sub-tiles past the expert's last row are skipped, so a short
-// tile costs MFMA issue in proportion to its real rows.
+// feature tile; 16-row sub-tiles past the expert's last row are skipped, so a
+// short tile costs MFMA issue in proportion to its real rows.
 //
 // Each workgroup (8 waves, two per SIMD) owns one token tile and one feature
 // tile.  The blockIdx -> work mapping is XCD aware: the dispatcher deals
@@ -23,22 +23,28 @@
 // of one token tile, which share its activation rows) sit on the same XCD and
 // its L2, and no XCD idles when the real tile count is below the grid bound.
 //
-// K loop (one K-step = 128 elements): the activation rows (kBM x 128 B, stored
-// with the 16-byte chunk index XOR-ed with the row's low 3 bits so that the
-// 128-bit LDS reads and writes of 8 lanes cover all banks), the feature tile's
-// packed weight tiles (16 KiB) and both operands' E8M0 scales travel global ->
-// registers -> LDS, double-buffered: step j's global loads for stage j+1 are
-// in flight during step j's MFMAs, then land in the other LDS buffer; one
-// barrier per K-step.  Every access is visible to the compiler, which
-// schedules the LDS reads among the MFMAs and waits on each load precisely.
+// K loop (one K-step = 128 elements): every operand of a K-step -- the
+// activation rows (kBM x 128 B, the 16-byte chunk index XOR-ed with the row's
+// low 3 bits so that 128-bit LDS reads of 8 lanes cover all banks), the
+// feature tile's 16 packed weight tiles and both operands' E8M0 scales --
+// travels from global memory straight into LDS with the gfx950 LDS-DMA loads
+// (global_load_lds_dword / _dwordx4: lane l of a wave writes 4 or 16 bytes at
+// M0 + 4l or M0 + 16l), into a ring of three stages: the loads of K-step j+2
+// are issued while step j is multiplied, so two steps of MFMA work cover the
+// HBM latency of the weights, and no register is spent on staging.  The DMA
+// loads are issued from inline assembly so that the compiler, which cannot
+// tell which LDS bytes a DMA writes, does not drain all of them before every
+// LDS read; instead each wave waits (s_waitcnt vmcnt) only for its own loads
+// of the stage about to be read, and one barrier per K-step publishes the
+// stage to all waves and retires the stage the next loads overwrite.
 //
-// Waves form a 2 (tokens) x 4 (features) grid: each wave owns the 16-row
-// sub-tiles {wm, wm+2, ..., wm+10} and 4 weight tiles (32 MFMAs per K-step
-// when all its sub-tiles are live); for the gate/up GEMM a wave's 4 tiles are
-// one 32-feature group of W1 and W3, so SwiGLU stays in its registers.  The number of live
-// sub-tiles is a compile-time parameter of the loop body, selected once per
-// wave, so the MFMA stream has no conditionals and only live accumulators are
-// allocated.
+// Waves form a 2 (tokens) x 4 (features) grid, wm = wave / 4 so that each
+// SIMD holds one wave of each token half: a wave owns the 16-row sub-tiles
+// {wm, wm+2, ..., wm+10} and 4 weight tiles (up to 24 MFMAs per K-step); for
+// the gate/up GEMM a wave's 4 tiles are one 32-feature group of W1 and W3, so
+// SwiGLU stays in its registers.  The number of live sub-tiles is a
+// compile-time parameter of the loop body, selected once per wave, so the
+// MFMA stream has no conditionals and only live accumulators are allocated.
 #include "common.h"
 
 namespace moe {
@@ -46,18 +52,26 @@ namespace {
 
 constexpr int kBM = 192;                 // token rows per tile (12 sub-tiles of 16)
 constexpr int kThreads = 512;            // 8 waves
+constexpr int kWaves = kThreads / 64;
 constexpr int kABytes = kBM * 128;       // activation rows of one K-step
 constexpr int kBBytes = 16384;           // 16 weight tiles of 1 KiB
+constexpr int kRing = 3;                 // LDS stages
 constexpr int kTileHdr = 256;            // tile count at offset 0, list at 256
+// DMA loads per wave per stage: 3 activation + 2 weight (dwordx4) for every
+// wave, plus one scale load (dword) on waves 0-6; the wait counts use the
+// smaller figure, which can only over-wait.
+constexpr int kOpsPerStageMin = 5;
 
 struct Stage {
   uint8_t a[kABytes];
   uint8_t b[kBBytes];
-  uint32_t as[256];  // activation scales: 4 blocks of the K-step per row (rows < kBM)
+  uint32_t as[kBM];  // activation scales: the 4 blocks of the K-step, one dword per row
   uint32_t bs[256];  // weight scales of the feature tile's tiles
 };
+static_assert(sizeof(Stage) % 16 == 0, "stage alignment");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // The FP4 B operand occupies the low 4 registers of the 8-register operand;
 // the upper half is left undefined so no registers are spent on it.
@@ -72,6 +86,43 @@ __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c, int sa, int sb)
 
 // Byte offset of 16-byte chunk c (0..7) of activation row r in a stage.
 __device__ __forceinline__ int a_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+// LDS-DMA: every lane of the wave loads 16 (or 4) bytes from its own global
+// address; lane l's bytes land at LDS byte address lds + 16 l (or 4 l).  `lds`
+// must be wave-uniform.  M0 carries the LDS address and is restored after; one
+// wait state separates the M0 write from the load that reads it.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Workgroup b is dispatched to XCD b % 8.  Give each XCD an equal contiguous
 // share of the W work items that exist (W is known on the device only; the
@@ -101,48 +152,32 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
   if (tid == 0) hdr[0] = total;
 }
 
-// Per-thread load plan and tile coordinates, computed once per workgroup.
-struct Plan {
-  const uint8_t* asrc[3];   // activation chunk sources (K-step 0)
-  const uint8_t* bsrc[2];   // weight chunk sources (K-step 0)
-  const uint32_t* sc;       // scale dword source (K-step 0): activation or weight
-  size_t bstep;             // weight bytes per K-step per chunk source
-  int bsstep;               // weight scale dwords per K-step
-  int J;                    // K-steps
-  int tid, wave, lane, wm, wn;
-  int nrows;                // rows of the tile (chunks of later rows are not loaded)
+// One wave's share of the DMA loads of a stage, at K-step 0; every source
+// advances by a fixed stride per K-step.  All LDS offsets are relative to the
+// stage and wave-uniform.
+struct Dma {
+  const uint8_t* a[3];  // this lane's activation chunk source, row groups w, w+8, w+16
+  const uint8_t* b[2];  // this lane's weight bytes, tiles 2w and 2w+1
+  const uint8_t* s;     // this lane's scale dword (waves 0-6)
+  int bstep;            // weight bytes per K-step
+  int sstep;            // scale bytes per K-step
+  uint32_t a_lds[3], b_lds[2], s_lds;
+  bool has_s;
 };
 
-// One stage in registers: 3 activation chunks, 2 weight chunks, 1 scale dword.
-struct Regs {
-  uint4 a[3], b[2];
-  uint32_t s;
-};
-
-__device__ __forceinline__ void gload(const Plan& p, Regs& R, int j) {
+__device__ __forceinline__ void issue_stage(const Dma& d, uint32_t stage_lds, int j) {
+  if (d.has_s) dma4(d.s + (size_t)j * d.sstep, stage_lds + d.s_lds);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) R.b[u] = *reinterpret_cast<const uint4*>(p.bsrc[u] + (size_t)j * p.bstep);
+  for (int u = 0; u < 3; ++u) dma16(d.a[u] + (size_t)j * 128, stage_lds + d.a_lds[u]);
 #pragma unroll
-  for (int u = 0; u < 3; ++u)
-    R.a[u] = (64 * u + (p.tid >> 3) < p.nrows)
-                 ? *reinterpret_cast<const uint4*>(p.asrc[u] + (size_t)j * 128) : make_uint4(0, 0, 0, 0);
-  R.s = (p.tid < 256) ? p.sc[j] : p.sc[(size_t)j * p.bsstep];
-}
-
-// Activation chunk u of thread tid: row 64u + (tid >> 3), logical chunk tid & 7.
-__device__ __forceinline__ void lstore(const Plan& p, Stage& s, const Regs& R) {
-#pragma unroll
-  for (int u = 0; u < 3; ++u)
-    *reinterpret_cast<uint4*>(&s.a[a_off(64 * u + (p.tid >> 3), p.tid & 7)]) = R.a[u];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&s.b[(kThreads * u + p.tid) * 16]) = R.b[u];
-  if (p.tid < 256) s.as[p.tid] = R.s; else s.bs[p.tid - 256] = R.s;
+  for (int u = 0; u < 2; ++u) dma16(d.b[u] + (size_t)j * d.bstep, stage_lds + d.b_lds[u]);
 }
 
 // One K-step of MFMAs for a wave with N live sub-tiles on LDS stage `cur`.
 template <bool kUp, int N>
-__device__ __forceinline__ void mfma_step(const Plan& p, const Stage& cur, v4f (&acc)[N][4]) {
-  const int lane = p.lane, g = lane >> 4, wm = p.wm, wn = p.wn;
+__device__ __forceinline__ void mfma_step(int lane, int wm, int wn, const Stage& cur,
+                                          v4f (&acc)[N][4]) {
+  const int g = lane >> 4;
   // this wave's 4 weight tiles: up = q-group wn (W1 0-15, W1 16-31, W3 0-15,
   // W3 16-31); down = q2-groups 2wn, 2wn+1 (2 tiles each)
   v8i b[4];
@@ -163,8 +198,8 @@ __device__ __forceinline__ void mfma_step(const Plan& p, const Stage& cur, v4f (
     }
   }
   // activation fragments one sub-tile ahead of the MFMAs; the scheduling
-  // fences keep at most two fragments live (registers) while the next
-  // fragment's LDS read overlaps this sub-tile's MFMAs
+  // fences keep at most two fragments live while the next fragment's LDS read
+  // overlaps this sub-tile's MFMAs
   auto read_a = [&](int i, v8i& a, int& sa) {
     const int row = 16 * (wm + 2 * i) + (lane & 15);
     const uint4 lo = *reinterpret_cast<const uint4*>(&cur.a[a_off(row, g)]);
@@ -187,31 +222,33 @@ __device__ __forceinline__ void mfma_step(const Plan& p, const Stage& cur, v4f (
 }
 
 template <bool kUp, int N>
-__device__ __forceinline__ void gemm_body(const Plan& p, Stage* st, int rows, int m0, int ft,
-                                          int I, int H, int QG2, uint8_t* __restrict__ hq,
-                                          uint8_t* __restrict__ hs, float* __restrict__ O) {
-  const int J = p.J;
+__device__ __forceinline__ void gemm_body(const Dma& d, Stage* st, int J, int lane, int wm, int wn,
+                                          int rows, int m0, int ft, int I, int H, int QG2,
+                                          uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
+                                          float* __restrict__ O) {
   v4f acc[N > 0 ? N : 1][4];
 #pragma unroll
   for (int i = 0; i < N; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // stage j+1 is loaded into registers while step j's MFMAs run, then written
-  // to the other LDS buffer; one barrier per K-step
-  Regs R;
-  gload(p, R, 0);
-  lstore(p, st[0], R);
-  __syncthreads();
+  const uint32_t ring = (uint32_t)(uintptr_t)(lds_u8*)st;
+  issue_stage(d, ring, 0);
+  if (J > 1) issue_stage(d, ring + (uint32_t)sizeof(Stage), 1);
   for (int j = 0; j < J; ++j) {
-    if (j + 1 < J) gload(p, R, j + 1);
-    if constexpr (N > 0) mfma_step<kUp, N>(p, st[j & 1], acc);
-    if (j + 1 < J) lstore(p, st[(j + 1) & 1], R);
+    // this wave's loads of stage j are done once at most one later stage's
+    // loads are outstanding; the barrier makes every wave's part visible and
+    // guarantees that stage j-1 (the slot stage j+2 refills) is no longer read
+    if (j + 1 < J)
+      wait_vmcnt<kOpsPerStageMin>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
+    if (j + 2 < J) issue_stage(d, ring + (uint32_t)(((j + 2) % kRing) * sizeof(Stage)), j + 2);
+    if constexpr (N > 0) mfma_step<kUp, N>(lane, wm, wn, st[j % kRing], acc);
   }
 
   // lane holds rows 4*(lane>>4)+v of each 16-row sub-tile, column lane&15 of each tile
-  const int lane = p.lane, wm = p.wm, wn = p.wn;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int rbase = 16 * (wm + 2 * i) + 4 * (lane >> 4);
@@ -259,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
     const uint8_t* __restrict__ act_s, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, int k, const int* __restrict__ hdr, int NF,
     int nblocks, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, float* __restrict__ O) {
-  __shared__ __align__(16) Stage st[2];
+  __shared__ __align__(16) Stage st[kRing];
   __shared__ int row_src[kBM];
   const int logical = xcd_work_item(blockIdx.x, hdr[0] * NF);
   if (logical < 0) return;
@@ -271,69 +308,86 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
   const int H = L.H, I = L.I;
   const int K = kUp ? H : I;  // reduction length
   const int QG2 = H / 32;     // 32-row groups of the down weights
+  // source row of each tile row; rows past the tile read row 0's data, whose
+  // products land in output rows that are never stored
   if (tid < kBM) row_src[tid] = (tid < rows) ? (kUp ? sorted_pair[m0 + tid] / k : m0 + tid) : -1;
   __syncthreads();
+  const int row0 = row_src[0];
 
-  Plan p;
-  p.tid = tid;
-  p.nrows = rows;
-  p.lane = tid & 63;
-  p.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
-  p.wm = p.wave & 1;
-  p.wn = p.wave >> 1;  // 0..3
-  p.J = K / 128;
-  // Activations: chunk u of thread tid = row 64u + (tid >> 3), logical 16-byte
-  // chunk tid & 7 (rows past the tile are not loaded).
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
+  const int wm = wave >> 2, wn = wave & 3;
+
+  Dma d;
+  // Activations: row group rg = wave + 8u holds rows 8rg..8rg+7, 1 KiB at LDS
+  // offset 1024 rg; lane l lands at row 8rg + l/8, physical chunk l%8, which
+  // holds logical chunk (l%8) ^ (l/8) (the row's low 3 bits are l/8).
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
-    const int r = 64 * u + (tid >> 3);
-    const int src = row_src[r] >= 0 ? row_src[r] : row_src[0];
-    p.asrc[u] = act + (size_t)src * K + (tid & 7) * 16;
+    const int rg = wave + kWaves * u;
+    const int r = 8 * rg + (lane >> 3);
+    const int src = row_src[r] >= 0 ? row_src[r] : row0;
+    d.a[u] = act + (size_t)src * K + (((lane & 7) ^ (lane >> 3)) << 4);
+    d.a_lds[u] = (uint32_t)(1024 * rg);
   }
-  // Weights: stage bytes (512u + tid) * 16, in packed-block order (up: 4 q-groups
-  // of 4 KiB; down: 8 q2-groups of 2 KiB; groups past H read group 0, unused).
+  // Weights: stage tiles 2w, 2w+1 (1 KiB each, lane order = packed order).
+  // up: tile index 4g + t = q-group 4ft + g of the feature tile, tile t;
+  // down: tile index 2g2 + t = q2-group 8ft + g2, tile t (groups past H
+  // read group 0, whose products are never stored).
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int ci = kThreads * u + tid;
+    const int ti = 2 * wave + u;
     if (kUp) {
-      p.bsrc[u] = packed + L.upw_block(e, 4 * ft + (ci >> 8), 0) + (ci & 255) * 16;
+      d.b[u] = packed + L.upw_block(e, 4 * ft + (ti >> 2), 0) + (ti & 3) * 1024 + lane * 16;
     } else {
-      const int g2 = 8 * ft + (ci >> 7);
-      p.bsrc[u] = packed + L.dnw_block(e, g2 < QG2 ? g2 : 0, 0) + (ci & 127) * 16;
+      const int g2 = 8 * ft + (ti >> 1);
+      d.b[u] = packed + L.dnw_block(e, g2 < QG2 ? g2 : 0, 0) + (ti & 1) * 1024 + lane * 16;
     }
+    d.b_lds[u] = (uint32_t)(kABytes + 1024 * ti);
   }
-  p.bstep = kUp ? 4096 : 2048;
-  // Scales: threads 0-255 fill as[tid] (activation scale dword of row tid, rows
-  // past kBM unused); threads 256-511 fill bs[d], d = tid - 256 (up: q-group
-  // d/64, lane d%64; down: q2-group d/32, lanes 2(d%32), 2(d%32)+1).
-  p.bsstep = kUp ? 64 : 32;
-  if (tid < 256) {
-    const int src = (tid < kBM && row_src[tid] >= 0) ? row_src[tid] : row_src[0];
-    p.sc = reinterpret_cast<const uint32_t*>(act_s + (size_t)src * (K / 32));
-  } else {
-    const int d = tid - 256;
+  d.bstep = kUp ? 4096 : 2048;
+  // Scales, one dword per lane: waves 0-2 the activation scales of rows
+  // 64w..64w+63 (as[row]); waves 3-6 the weight scales: up: q-group w-3, its
+  // 64 lane dwords (bs[64g + lane]); down: q2-groups 2(w-3), 2(w-3)+1, 32
+  // dwords each (bs[32 g2 + d]).
+  d.has_s = wave < 7;
+  d.s = act_s;
+  d.sstep = 4;
+  d.s_lds = 0;
+  if (wave < 3) {
+    const int r = 64 * wave + lane;
+    const int src = row_src[r] >= 0 ? row_src[r] : row0;
+    d.s = act_s + (size_t)src * (K / 32);
+    d.sstep = 4;
+    d.s_lds = (uint32_t)(kABytes + kBBytes + 256 * wave);
+  } else if (wave < 7) {
+    const int gw = wave - 3;
     if (kUp) {
-      p.sc = reinterpret_cast<const uint32_t*>(packed + L.ups_block(e, 4 * ft + (d >> 6), 0)) + (d & 63);
+      d.s = packed + L.ups_block(e, 4 * ft + gw, 0) + lane * 4;
+      d.sstep = 256;
     } else {
-      const int g2 = 8 * ft + (d >> 5);
-      p.sc = reinterpret_cast<const uint32_t*>(packed + L.dns_block(e, g2 < QG2 ? g2 : 0, 0)) + (d & 31);
+      const int g2 = 8 * ft + 2 * gw + (lane >> 5);
+      d.s = packed + L.dns_block(e, g2 < QG2 ? g2 : 0, 0) + (lane & 31) * 4;
+      d.sstep = 128;
     }
+    d.s_lds = (uint32_t)(kABytes + kBBytes + kBM * 4 + 256 * gw);
   }
 
+  const int J = K / 128;
   const int nsub = (rows + 15) / 16;  // live 16-row sub-tiles of the tile
   int nact = 0;                       // this wave's live sub-tiles: i = 0..nact-1
 #pragma unroll
   for (int i = 0; i < kBM / 32; ++i)
-    if (p.wm + 2 * i < nsub) nact = i + 1;
+    if (wm + 2 * i < nsub) nact = i + 1;
   nact = __builtin_amdgcn_readfirstlane(nact);
   switch (nact) {
-    case 0: gemm_body<kUp, 0>(p, st, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 1: gemm_body<kUp, 1>(p, st, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 2: gemm_body<kUp, 2>(p, st, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 3: gemm_body<kUp, 3>(p, st, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 4: gemm_body<kUp, 4>(p, st, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 5: gemm_body<kUp, 5>(p, st, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    default: gemm_body<kUp, 6>(p, st, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 0: gemm_body<kUp, 0>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 1: gemm_body<kUp, 1>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 2: gemm_body<kUp, 2>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 3: gemm_body<kUp, 3>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 4: gemm_body<kUp, 4>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 5: gemm_body<kUp, 5>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    default: gemm_body<kUp, 6>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
   }
 }
 
