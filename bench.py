@@ -163,7 +163,7 @@ def main():
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=dev)
     O = torch.empty((P, H), dtype=torch.float32, device=dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
-    stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, k, E), 256),
+    stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, k, E, H, I), 256),
                            dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 

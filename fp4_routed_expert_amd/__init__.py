@@ -135,8 +135,12 @@ def prepack_weights(w1, s1, w3, s3, w2, s2) -> PackedWeights:
     return PackedWeights(buffer=buf, desc=desc)
 
 
-def _stage_ws(T, k, E, dev, workspace):
-    need = _lib.lib().moe_fp4_stage_workspace_size(T, k, E)
+def stage_workspace_size(T: int, k: int, E: int, H: int, I: int) -> int:
+    return int(_lib.lib().moe_fp4_stage_workspace_size(T, k, E, H, I))
+
+
+def _stage_ws(T, k, pw, dev, workspace):
+    need = stage_workspace_size(T, k, pw.E, pw.H, pw.I)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     return workspace
@@ -151,7 +155,7 @@ def expert_up(pw: PackedWeights, xq, xs, offsets, sorted_pair, T: int, k: int, f
         hq = torch.empty((P, pw.I), dtype=torch.uint8, device=dev)
     if hs is None:
         hs = torch.empty((P, pw.I // 32), dtype=torch.uint8, device=dev)
-    workspace = _stage_ws(T, k, pw.E, dev, workspace)
+    workspace = _stage_ws(T, k, pw, dev, workspace)
     _lib.check(_lib.lib().moe_fp4_expert_up(
         ctypes.byref(pw.desc), _ptr(xq), _ptr(xs), _ptr(offsets), _ptr(sorted_pair), T, k, _ptr(hq),
         _ptr(hs), _ptr(workspace), workspace.numel(), flags, _stream(xq)), "moe_fp4_expert_up")
@@ -164,7 +168,7 @@ def expert_down(pw: PackedWeights, hq, hs, offsets, T: int, k: int, flags: int =
     dev = hq.device
     if O is None:
         O = torch.empty((T * k, pw.H), dtype=torch.float32, device=dev)
-    workspace = _stage_ws(T, k, pw.E, dev, workspace)
+    workspace = _stage_ws(T, k, pw, dev, workspace)
     _lib.check(_lib.lib().moe_fp4_expert_down(
         ctypes.byref(pw.desc), _ptr(hq), _ptr(hs), _ptr(offsets), T, k, _ptr(O), _ptr(workspace),
         workspace.numel(), flags, _stream(hq)), "moe_fp4_expert_down")

@@ -58,7 +58,7 @@ SIGNATURES = {
     "moe_fp4_packed_weight_bytes": (_SZ, [_I32, _I32, _I32]),
     "moe_fp4_prepack_weights": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _SZ,
                                                _WP, _P]),
-    "moe_fp4_stage_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "moe_fp4_stage_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_fp4_expert_up": (ctypes.c_int, [_WP, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _U32, _P]),
     "moe_fp4_expert_down": (ctypes.c_int, [_WP, _P, _P, _P, _I32, _I32, _P, _P, _SZ, _U32, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),

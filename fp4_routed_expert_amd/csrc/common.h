@@ -166,7 +166,7 @@ hipError_t launch_up_decode(const uint8_t* packed, const PackedLayout& L, const 
 hipError_t launch_down_decode(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
                               const uint8_t* hs, const int32_t* offsets, float* O,
                               hipStream_t s);
-size_t prefill_tile_bytes(long P, int E);
+size_t prefill_stage_bytes(long P, int E, int H, int I);
 hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
                              const uint8_t* xs, const int32_t* offsets,
                              const int32_t* sorted_pair, int T, int k, uint8_t* hq, uint8_t* hs,

@@ -29,14 +29,22 @@
 // feature tile's 16 packed weight tiles and both operands' E8M0 scales --
 // travels from global memory straight into LDS with the gfx950 LDS-DMA loads
 // (global_load_lds_dword / _dwordx4: lane l of a wave writes 4 or 16 bytes at
-// M0 + 4l or M0 + 16l), into a ring of three stages: the loads of K-step j+2
-// are issued while step j is multiplied, so two steps of MFMA work cover the
-// HBM latency of the weights, and no register is spent on staging.  The DMA
-// loads are issued from inline assembly so that the compiler, which cannot
-// tell which LDS bytes a DMA writes, does not drain all of them before every
-// LDS read; instead each wave waits (s_waitcnt vmcnt) only for its own loads
-// of the stage about to be read, and one barrier per K-step publishes the
-// stage to all waves and retires the stage the next loads overwrite.
+// M0 + 4l or M0 + 16l), into a ring of three stages, so no register is spent
+// on staging.  Every wave issues the same six loads per stage (three
+// activation row groups, two weight tiles, one scale dword) and one stage per
+// K-step, past the last K-step too (the last stage again, never read), so the
+// number of its loads outstanding after any stage is a constant and the wait
+// for a stage is one fixed s_waitcnt vmcnt.  The DMA loads are issued from
+// inline assembly so that the compiler, which cannot tell which LDS bytes a
+// DMA writes, does not drain them before every LDS read.
+//
+// A K-step is software-pipelined across the LDS ring: its weight fragments
+// and first half of activation fragments (the head) were read from LDS during
+// the previous step; the rest (the tail) are read at its start, behind the
+// head's MFMAs; midway, one barrier publishes the next stage and retires the
+// current slot, which is refilled at once, and the next head is read behind
+// the tail's MFMAs.  So LDS reads, DMA issue and the barrier all overlap
+// MFMA work, and the loop body has no branches.
 //
 // Waves form a 2 (tokens) x 4 (features) grid, wm = wave / 4 so that each
 // SIMD holds one wave of each token half: a wave owns the 16-row sub-tiles
@@ -52,15 +60,15 @@ namespace {
 
 constexpr int kBM = 192;                 // token rows per tile (12 sub-tiles of 16)
 constexpr int kThreads = 512;            // 8 waves
-constexpr int kWaves = kThreads / 64;
 constexpr int kABytes = kBM * 128;       // activation rows of one K-step
 constexpr int kBBytes = 16384;           // 16 weight tiles of 1 KiB
 constexpr int kRing = 3;                 // LDS stages
 constexpr int kTileHdr = 256;            // tile count at offset 0, list at 256
-// DMA loads per wave per stage: 3 activation + 2 weight (dwordx4) for every
-// wave, plus one scale load (dword) on waves 0-6; the wait counts use the
-// smaller figure, which can only over-wait.
-constexpr int kOpsPerStageMin = 5;
+// DMA loads per wave per stage: 3 activation row groups and 2 weight tiles
+// (dwordx4) on every wave, plus one scale load on waves 0-3 (activation scale
+// dwords on waves 0-2, all weight scales as one dwordx4 on wave 3).  Waits use
+// the smaller count, which can only over-wait.
+constexpr int kOps = 5;
 
 struct Stage {
   uint8_t a[kABytes];
@@ -153,72 +161,115 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
 }
 
 // One wave's share of the DMA loads of a stage, at K-step 0; every source
-// advances by a fixed stride per K-step.  All LDS offsets are relative to the
+// advances by a fixed stride per K-step.  LDS offsets are relative to the
 // stage and wave-uniform.
 struct Dma {
-  const uint8_t* a[3];  // this lane's activation chunk source, row groups w, w+8, w+16
-  const uint8_t* b[2];  // this lane's weight bytes, tiles 2w and 2w+1
-  const uint8_t* s;     // this lane's scale dword (waves 0-6)
-  int bstep;            // weight bytes per K-step
-  int sstep;            // scale bytes per K-step
+  const uint8_t* a[3];  // this lane's activation chunk sources
+  const uint8_t* b[2];  // this lane's weight bytes
+  const uint8_t* s;     // this lane's scale source (4 or 16 bytes)
   uint32_t a_lds[3], b_lds[2], s_lds;
-  bool has_s;
+  int bstep;            // weight bytes per K-step
+  size_t sstep;         // scale bytes per K-step
+  int skind;            // 0: no scale load, 1: dword, 2: dwordx4 (wave-uniform)
 };
 
 __device__ __forceinline__ void issue_stage(const Dma& d, uint32_t stage_lds, int j) {
-  if (d.has_s) dma4(d.s + (size_t)j * d.sstep, stage_lds + d.s_lds);
+  if (d.skind == 1)
+    dma4(d.s + (size_t)j * d.sstep, stage_lds + d.s_lds);
+  else if (d.skind == 2)
+    dma16(d.s + (size_t)j * d.sstep, stage_lds + d.s_lds);
 #pragma unroll
   for (int u = 0; u < 3; ++u) dma16(d.a[u] + (size_t)j * 128, stage_lds + d.a_lds[u]);
 #pragma unroll
   for (int u = 0; u < 2; ++u) dma16(d.b[u] + (size_t)j * d.bstep, stage_lds + d.b_lds[u]);
 }
 
-// One K-step of MFMAs for a wave with N live sub-tiles on LDS stage `cur`.
-template <bool kUp, int N>
-__device__ __forceinline__ void mfma_step(int lane, int wm, int wn, const Stage& cur,
-                                          v4f (&acc)[N][4]) {
-  const int g = lane >> 4;
-  // this wave's 4 weight tiles: up = q-group wn (W1 0-15, W1 16-31, W3 0-15,
-  // W3 16-31); down = q2-groups 2wn, 2wn+1 (2 tiles each)
-  v8i b[4];
+// Operand fragments of one K-step for a wave with N live sub-tiles: its 4
+// weight tiles (up: q-group wn = W1 rows 0-15, W1 16-31, W3 0-15, W3 16-31;
+// down: q2-groups 2wn, 2wn+1, 2 tiles each) and the activation fragments of
+// its sub-tiles wm, wm+2, ...  A operand (fp8) of the 16x16x128 scaled MFMA:
+// lane l holds row l%16, K bytes [16g, 16g+16) and [64+16g, 64+16g+16) for
+// g = l/16, and supplies the E8M0 scale of the row's block g.  The head holds
+// the weight fragments and the first kHead activation fragments, read one
+// step ahead; the tail the remaining activation fragments, read at the start
+// of the step that uses them.
+template <int N>
+struct FragsShape {
+  static constexpr int kHead = (N + 1) / 2;
+  static constexpr int kTail = N - kHead;
+};
+
+template <int N>
+struct Head {
+  uint4 b[4];
   int sb[4];
+  v8i a[FragsShape<N>::kHead > 0 ? FragsShape<N>::kHead : 1];
+  int sa[FragsShape<N>::kHead > 0 ? FragsShape<N>::kHead : 1];
+};
+
+template <int N>
+struct Tail {
+  v8i a[FragsShape<N>::kTail > 0 ? FragsShape<N>::kTail : 1];
+  int sa[FragsShape<N>::kTail > 0 ? FragsShape<N>::kTail : 1];
+};
+
+__device__ __forceinline__ void read_a(v8i& a, int& sa, int lane, int row, const Stage& ca) {
+  const int g = lane >> 4;
+  const uint4 lo = *reinterpret_cast<const uint4*>(&ca.a[a_off(row, g)]);
+  const uint4 hi = *reinterpret_cast<const uint4*>(&ca.a[a_off(row, g + 4)]);
+  a = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  sa = (int)((ca.as[row] >> (8 * g)) & 0xFFu);
+}
+
+template <bool kUp, int N>
+__device__ __forceinline__ void read_head(Head<N>& f, int lane, int wm, int wn, const Stage& c) {
+  const Stage& ca = c;
+  const Stage& cb = c;
   if (kUp) {
-    const uint32_t w = cur.bs[wn * 64 + lane];
+    const uint32_t w = cb.bs[wn * 64 + lane];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      sb[t] = (int)((w >> (8 * t)) & 0xFFu);
-      b[t] = widen_fp4(*reinterpret_cast<const uint4*>(&cur.b[wn * 4096 + t * 1024 + lane * 16]));
+      f.sb[t] = (int)((w >> (8 * t)) & 0xFFu);
+      f.b[t] = *reinterpret_cast<const uint4*>(&cb.b[wn * 4096 + t * 1024 + lane * 16]);
     }
   } else {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int g2 = 2 * wn + (t >> 1);
-      sb[t] = (int)((cur.bs[g2 * 32 + (lane >> 1)] >> (16 * (lane & 1) + 8 * (t & 1))) & 0xFFu);
-      b[t] = widen_fp4(*reinterpret_cast<const uint4*>(&cur.b[g2 * 2048 + (t & 1) * 1024 + lane * 16]));
+      f.sb[t] = (int)((cb.bs[g2 * 32 + (lane >> 1)] >> (16 * (lane & 1) + 8 * (t & 1))) & 0xFFu);
+      f.b[t] = *reinterpret_cast<const uint4*>(&cb.b[g2 * 2048 + (t & 1) * 1024 + lane * 16]);
     }
   }
-  // activation fragments one sub-tile ahead of the MFMAs; the scheduling
-  // fences keep at most two fragments live while the next fragment's LDS read
-  // overlaps this sub-tile's MFMAs
-  auto read_a = [&](int i, v8i& a, int& sa) {
-    const int row = 16 * (wm + 2 * i) + (lane & 15);
-    const uint4 lo = *reinterpret_cast<const uint4*>(&cur.a[a_off(row, g)]);
-    const uint4 hi = *reinterpret_cast<const uint4*>(&cur.a[a_off(row, g + 4)]);
-    a = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    sa = (int)((cur.as[row] >> (8 * g)) & 0xFFu);
-  };
-  v8i a_cur, a_nxt;
-  int sa_cur, sa_nxt;
-  read_a(0, a_cur, sa_cur);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i + 1 < N) read_a(i + 1, a_nxt, sa_nxt);
+  for (int i = 0; i < FragsShape<N>::kHead; ++i)
+    read_a(f.a[i], f.sa[i], lane, 16 * (wm + 2 * i) + (lane & 15), ca);
+}
+
+template <int N>
+__device__ __forceinline__ void read_tail(Tail<N>& f, int lane, int wm, const Stage& ca) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = mfma_fp8_fp4(a_cur, b[t], acc[i][t], sa_cur, sb[t]);
-    __builtin_amdgcn_sched_barrier(0);
-    a_cur = a_nxt;
-    sa_cur = sa_nxt;
-  }
+  for (int i = 0; i < FragsShape<N>::kTail; ++i)
+    read_a(f.a[i], f.sa[i], lane, 16 * (wm + 2 * (FragsShape<N>::kHead + i)) + (lane & 15), ca);
+}
+
+template <int N>
+__device__ __forceinline__ void mfma_head(const Head<N>& f, v4f (&acc)[N][4]) {
+#pragma unroll
+  for (int i = 0; i < FragsShape<N>::kHead; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc[i][t] = mfma_fp8_fp4(f.a[i], widen_fp4(f.b[t]), acc[i][t], f.sa[i], f.sb[t]);
+}
+
+template <int N>
+__device__ __forceinline__ void mfma_tail(const Head<N>& h, const Tail<N>& f, v4f (&acc)[N][4]) {
+#pragma unroll
+  for (int i = 0; i < FragsShape<N>::kTail; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v4f& c = acc[FragsShape<N>::kHead + i][t];
+      c = mfma_fp8_fp4(f.a[i], widen_fp4(h.b[t]), c, f.sa[i], h.sb[t]);
+    }
 }
 
 template <bool kUp, int N>
@@ -233,20 +284,45 @@ __device__ __forceinline__ void gemm_body(const Dma& d, Stage* st, int J, int la
     for (int t = 0; t < 4; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t ring = (uint32_t)(uintptr_t)(lds_u8*)st;
-  issue_stage(d, ring, 0);
-  if (J > 1) issue_stage(d, ring + (uint32_t)sizeof(Stage), 1);
-  for (int j = 0; j < J; ++j) {
-    // this wave's loads of stage j are done once at most one later stage's
-    // loads are outstanding; the barrier makes every wave's part visible and
-    // guarantees that stage j-1 (the slot stage j+2 refills) is no longer read
-    if (j + 1 < J)
-      wait_vmcnt<kOpsPerStageMin>();
-    else
-      wait_vmcnt<0>();
+  // stage s goes to slot s % kRing; stages past the last load the last again
+  auto issue = [&](int s) {
+    issue_stage(d, ring + (uint32_t)(s % kRing) * (uint32_t)sizeof(Stage), min(s, J - 1));
+  };
+  // Step j multiplies stage j from registers (head hc read during step j-1,
+  // tail read here).  Stages issued before its barrier run up to j + 2, so
+  // stage j+1 is complete once at most one stage of this wave's loads is
+  // outstanding; the barrier then publishes it to every wave and retires slot
+  // j % kRing (every wave's reads of stage j precede it), which takes stage
+  // j + 3.
+  auto step = [&](int j, Head<N>& hc, Head<N>& hn) {
+    Tail<N> tl;
+    if constexpr (N > 0) read_tail<N>(tl, lane, wm, st[j % kRing]);
+    if constexpr (N > 0) mfma_head<N>(hc, acc);
+    wait_vmcnt<kOps>();
     __syncthreads();
-    if (j + 2 < J) issue_stage(d, ring + (uint32_t)(((j + 2) % kRing) * sizeof(Stage)), j + 2);
-    if constexpr (N > 0) mfma_step<kUp, N>(lane, wm, wn, st[j % kRing], acc);
+    if constexpr (N > 0) read_head<kUp, N>(hn, lane, wm, wn, st[(j + 1) % kRing]);
+    issue(j + kRing);
+    if constexpr (N > 0) mfma_tail<N>(hc, tl, acc);
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  Head<N> h0, h1;
+  wait_vmcnt<2 * kOps>();
+  __syncthreads();
+  if constexpr (N > 0) read_head<kUp, N>(h0, lane, wm, wn, st[0]);
+  int j = 0;
+  if (J & 1) {  // odd J: one step first, so the loop below takes steps in pairs
+    step(0, h0, h1);
+    h0 = h1;
+    j = 1;
   }
+  for (; j < J; j += 2) {
+    step(j, h0, h1);
+    step(j + 1, h1, h0);
+  }
+  // no LDS-DMA may still be writing when the workgroup's LDS is released
+  wait_vmcnt<0>();
 
   // lane holds rows 4*(lane>>4)+v of each 16-row sub-tile, column lane&15 of each tile
 #pragma unroll
@@ -287,13 +363,28 @@ __device__ __forceinline__ void gemm_body(const Dma& d, Stage* st, int J, int la
   }
 }
 
+// Activation scales by K-step: sT[j][p] = the dword of E8M0 codes of K-step j
+// (4 blocks of 32) of sorted row p, taken from row sorted_pair[p] / k of the
+// token-order scales (gate/up), or from row p (down, sorted_pair null).  A
+// tile's rows are consecutive sorted rows, so each K-step's scale loads then
+// read one contiguous run instead of one dword from each of 192 rows.
+__global__ __launch_bounds__(256) void scales_by_step_kernel(const uint32_t* __restrict__ src,
+                                                             int J, const int32_t* __restrict__ sorted_pair,
+                                                             int k, long P, uint32_t* __restrict__ sT) {
+  const long p = (long)blockIdx.x * 256 + threadIdx.x;
+  const int j = blockIdx.y;
+  if (p >= P) return;
+  const long row = sorted_pair ? (long)(sorted_pair[p] / k) : p;
+  sT[(size_t)j * P + p] = src[(size_t)row * J + j];
+}
+
 // kUp: gate/up GEMM (A = x rows gathered by token, K = H; B = W1/W3; epilogue
 // SwiGLU + MXFP8 of h).  !kUp: down GEMM (A = h rows in sorted order, K = I;
 // B = W2; epilogue fp32 store of O).
 template <bool kUp>
 __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
     const uint8_t* __restrict__ packed, PackedLayout L, const uint8_t* __restrict__ act,
-    const uint8_t* __restrict__ act_s, const int32_t* __restrict__ offsets,
+    const uint32_t* __restrict__ sT, long P, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, int k, const int* __restrict__ hdr, int NF,
     int nblocks, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, float* __restrict__ O) {
   __shared__ __align__(16) Stage st[kRing];
@@ -319,21 +410,22 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
   const int wm = wave >> 2, wn = wave & 3;
 
   Dma d;
-  // Activations: row group rg = wave + 8u holds rows 8rg..8rg+7, 1 KiB at LDS
-  // offset 1024 rg; lane l lands at row 8rg + l/8, physical chunk l%8, which
-  // holds logical chunk (l%8) ^ (l/8) (the row's low 3 bits are l/8).
+  // Activations: row group rg = wave + 8u (u < 3) holds rows 8rg..8rg+7,
+  // 1 KiB at stage offset 1024 rg; lane l lands at row 8rg + l/8, physical
+  // chunk l%8, which holds logical chunk (l%8) ^ (l/8) (the row's low 3 bits
+  // are l/8).
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
-    const int rg = wave + kWaves * u;
+    const int rg = wave + 8 * u;
     const int r = 8 * rg + (lane >> 3);
     const int src = row_src[r] >= 0 ? row_src[r] : row0;
     d.a[u] = act + (size_t)src * K + (((lane & 7) ^ (lane >> 3)) << 4);
     d.a_lds[u] = (uint32_t)(1024 * rg);
   }
   // Weights: stage tiles 2w, 2w+1 (1 KiB each, lane order = packed order).
-  // up: tile index 4g + t = q-group 4ft + g of the feature tile, tile t;
-  // down: tile index 2g2 + t = q2-group 8ft + g2, tile t (groups past H
-  // read group 0, whose products are never stored).
+  // up: tile index 4g + t = q-group 4ft + g, tile t; down: tile index
+  // 2g2 + t = q2-group 8ft + g2, tile t (groups past H read group 0, whose
+  // products are never stored).
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int ti = 2 * wave + u;
@@ -346,31 +438,34 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
     d.b_lds[u] = (uint32_t)(kABytes + 1024 * ti);
   }
   d.bstep = kUp ? 4096 : 2048;
-  // Scales, one dword per lane: waves 0-2 the activation scales of rows
-  // 64w..64w+63 (as[row]); waves 3-6 the weight scales: up: q-group w-3, its
-  // 64 lane dwords (bs[64g + lane]); down: q2-groups 2(w-3), 2(w-3)+1, 32
-  // dwords each (bs[32 g2 + d]).
-  d.has_s = wave < 7;
-  d.s = act_s;
-  d.sstep = 4;
-  d.s_lds = 0;
+  // Scales.  Waves 0-2: activation scale dwords of rows 64w..64w+63 (as[row])
+  // from the by-step array, one contiguous run per K-step (rows past the
+  // tile read its last row).  Wave 3: all weight scales of the K-step as one
+  // dwordx4 load, 16 bytes per lane: up: lanes 16g..16g+15 take q-group
+  // 4ft + g's 256 bytes (bs[64g + d]); down: lanes 8g2..8g2+7 take q2-group
+  // 8ft + g2's 128 bytes (bs[32 g2 + d]).
   if (wave < 3) {
     const int r = 64 * wave + lane;
-    const int src = row_src[r] >= 0 ? row_src[r] : row0;
-    d.s = act_s + (size_t)src * (K / 32);
-    d.sstep = 4;
+    d.s = reinterpret_cast<const uint8_t*>(sT + m0 + min(r, rows - 1));
+    d.sstep = (size_t)P * 4;
     d.s_lds = (uint32_t)(kABytes + kBBytes + 256 * wave);
-  } else if (wave < 7) {
-    const int gw = wave - 3;
+    d.skind = 1;
+  } else if (wave == 3) {
     if (kUp) {
-      d.s = packed + L.ups_block(e, 4 * ft + gw, 0) + lane * 4;
+      d.s = packed + L.ups_block(e, 4 * ft + (lane >> 4), 0) + (lane & 15) * 16;
       d.sstep = 256;
     } else {
-      const int g2 = 8 * ft + 2 * gw + (lane >> 5);
-      d.s = packed + L.dns_block(e, g2 < QG2 ? g2 : 0, 0) + (lane & 31) * 4;
+      const int g2 = 8 * ft + (lane >> 3);
+      d.s = packed + L.dns_block(e, g2 < QG2 ? g2 : 0, 0) + (lane & 7) * 16;
       d.sstep = 128;
     }
-    d.s_lds = (uint32_t)(kABytes + kBBytes + kBM * 4 + 256 * gw);
+    d.s_lds = (uint32_t)(kABytes + kBBytes + kBM * 4);
+    d.skind = 2;
+  } else {
+    d.s = nullptr;
+    d.sstep = 0;
+    d.s_lds = 0;
+    d.skind = 0;
   }
 
   const int J = K / 128;
@@ -393,32 +488,48 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
 
 long max_tiles(long P, int E) { return (P + kBM - 1) / kBM + E; }
 
+size_t align256_(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// workspace: tile header and list, then the by-step activation scales
+size_t tile_list_bytes(long P, int E) { return align256_(kTileHdr + (size_t)max_tiles(P, E) * 8); }
+
 }  // namespace
 
-size_t prefill_tile_bytes(long P, int E) { return kTileHdr + (size_t)max_tiles(P, E) * 8; }
+size_t prefill_stage_bytes(long P, int E, int H, int I) {
+  const int Jmax = (H > I ? H : I) / 128;
+  return tile_list_bytes(P, E) + align256_((size_t)P * Jmax * 4);
+}
 
 hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
                              const uint8_t* xs, const int32_t* offsets,
                              const int32_t* sorted_pair, int T, int k, uint8_t* hq, uint8_t* hs,
                              void* tile_ws, hipStream_t s) {
+  const long P = (long)T * k;
   int* hdr = static_cast<int*>(tile_ws);
+  uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, L.E, hdr);
+  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 255) / 256), (unsigned)L.J), dim3(256),
+                     0, s, reinterpret_cast<const uint32_t*>(xs), L.J, sorted_pair, k, P, sT);
   const int NF = L.I / 128;
-  const long nb = (max_tiles((long)T * k, L.E) * NF + 7) / 8 * 8;
+  const long nb = (max_tiles(P, L.E) * NF + 7) / 8 * 8;
   hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)nb), dim3(kThreads), 0, s, packed, L,
-                     xq, xs, offsets, sorted_pair, k, hdr, NF, (int)nb, hq, hs, (float*)nullptr);
+                     xq, sT, P, offsets, sorted_pair, k, hdr, NF, (int)nb, hq, hs, (float*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
                                const uint8_t* hs, const int32_t* offsets, int T, int k, float* O,
                                void* tile_ws, hipStream_t s) {
+  const long P = (long)T * k;
   int* hdr = static_cast<int*>(tile_ws);
+  uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, L.E, hdr);
+  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 255) / 256), (unsigned)L.J2), dim3(256),
+                     0, s, reinterpret_cast<const uint32_t*>(hs), L.J2, (const int32_t*)nullptr, k, P, sT);
   const int NF = (L.H + 255) / 256;
-  const long nb = (max_tiles((long)T * k, L.E) * NF + 7) / 8 * 8;
+  const long nb = (max_tiles(P, L.E) * NF + 7) / 8 * 8;
   hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)nb), dim3(kThreads), 0, s, packed,
-                     L, hq, hs, offsets, (const int32_t*)nullptr, k, hdr, NF, (int)nb,
+                     L, hq, sT, P, offsets, (const int32_t*)nullptr, k, hdr, NF, (int)nb,
                      (uint8_t*)nullptr, (uint8_t*)nullptr, O);
   return hipGetLastError();
 }

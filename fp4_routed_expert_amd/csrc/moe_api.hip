@@ -60,8 +60,8 @@ int select_path(int64_t P, int E, uint32_t flags) {
   return P <= 16 * (int64_t)E ? 0 : 1;
 }
 
-size_t stage_ws_bytes(int32_t T, int32_t k, int32_t E) {
-  return align256(prefill_tile_bytes((long)T * k, E));
+size_t stage_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+  return align256(prefill_stage_bytes((long)T * k, E, H, I));
 }
 
 struct FwdCarve {
@@ -75,7 +75,7 @@ FwdCarve carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
   c.hs = align256(c.hq + P * I);
   c.O = align256(c.hs + P * (I / 32));
   c.stage = align256(c.O + P * H * sizeof(float));
-  c.total = align256(c.stage + stage_ws_bytes(T, k, E));
+  c.total = align256(c.stage + stage_ws_bytes(T, k, E, H, I));
   return c;
 }
 
@@ -191,9 +191,9 @@ moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1, const
   return MOE_OK;
 }
 
-size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E) {
-  if (check_tek(T, E, k) != MOE_OK) return 0;
-  return stage_ws_bytes(T, k, E);
+size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+  if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
+  return stage_ws_bytes(T, k, E, H, I);
 }
 
 moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, const uint8_t* xs,
@@ -210,7 +210,7 @@ moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, co
   if (!xq || !xs || !expert_offsets || !sorted_pair || !hq || !hs) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(xq, 16) || !aligned(hq, 16) || !aligned(xs, 4) || !aligned(hs, 4))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!workspace || workspace_bytes < stage_ws_bytes(T, k, w->E)) return MOE_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < stage_ws_bytes(T, k, w->E, w->H, w->I)) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   const PackedLayout L(w->E, w->H, w->I);
   const uint8_t* pk = static_cast<const uint8_t*>(w->packed);
@@ -233,7 +233,7 @@ moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, 
   if (T == 0) return MOE_OK;
   if (!hq || !hs || !expert_offsets || !O) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(hq, 16) || !aligned(O, 16) || !aligned(hs, 4)) return MOE_ERR_INVALID_ARGUMENT;
-  if (!workspace || workspace_bytes < stage_ws_bytes(T, k, w->E)) return MOE_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < stage_ws_bytes(T, k, w->E, w->H, w->I)) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   const PackedLayout L(w->E, w->H, w->I);
   const uint8_t* pk = static_cast<const uint8_t*>(w->packed);

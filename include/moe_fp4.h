@@ -157,9 +157,11 @@ moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1,
  *   xq [T, H], xs [T, H/32] from moe_quant_act_mxfp8
  *   expert_offsets [E+1], sorted_pair [T*k] from moe_sort_permute
  *   hq [T*k, I] (out), hs [T*k, I/32] (out), rows in sorted order
- *   workspace >= moe_fp4_stage_workspace_size(T, k, E)
+ *   workspace >= moe_fp4_stage_workspace_size(T, k, E, H, I), 256-aligned
+ *   (the prefill path's tile list and its activation scales rearranged by
+ *   K-step; contents on entry are ignored)
  */
-size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E);
+size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I);
 moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w /*(host)*/,
                                const uint8_t* xq, const uint8_t* xs,
                                const int32_t* expert_offsets, const int32_t* sorted_pair,

@@ -113,7 +113,9 @@ def test_forward_argument_errors():
     small.packed_bytes -= 1
     assert fwd(ctypes.byref(small), A, A, A, A, A, A, 16, 2, A, A, ws, 0, NUL) == INV
     up = L.moe_fp4_expert_up
-    sws = L.moe_fp4_stage_workspace_size(16, 2, 8)
+    sws = L.moe_fp4_stage_workspace_size(16, 2, 8, 256, 128)
+    assert sws >= 32 * (256 // 128) * 4          # the activation scales by K-step
+    assert L.moe_fp4_stage_workspace_size(16, 2, 8, 200, 128) == 0
     assert up(ctypes.byref(d), A, A, A, A, 16, 2, A, A, A, sws - 1, 0, NUL) == WSE
     assert L.moe_combine(A, A, A, 4, 2, 250, A, NUL) == UNS       # H % 4
     assert L.moe_combine(A, A, A, 4, 0, 256, A, NUL) == INV
