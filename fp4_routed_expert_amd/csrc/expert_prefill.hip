@@ -95,33 +95,65 @@ __device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c, int sa, int sb)
 // Byte offset of 16-byte chunk c (0..7) of activation row r in a stage.
 __device__ __forceinline__ int a_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
-// LDS-DMA: every lane of the wave loads 16 (or 4) bytes from its own global
-// address; lane l's bytes land at LDS byte address lds + 16 l (or 4 l).  `lds`
-// must be wave-uniform.  M0 carries the LDS address and is restored after; one
-// wait state separates the M0 write from the load that reads it.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+// LDS-DMA with a uniform 64-bit base in SGPRs and a per-lane 32-bit offset
+// (the saddr form): every lane loads 16 (or 4) bytes from base + its offset;
+// lane l's bytes land at LDS byte address m0 + 16 l (or 4 l).  The LDS
+// addresses are wave-uniform.  M0 is restored after; one wait state
+// separates each M0 write from the load that reads it.
+__device__ __forceinline__ void dma_x4(const uint8_t* base, uint32_t off, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(g), "s"(lds)
+      : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
 
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+__device__ __forceinline__ void dma_x1(const uint8_t* base, uint32_t off, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
+      "global_load_lds_dword %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(g), "s"(lds)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// The five 16-byte loads of a wave's stage (three activation row groups from
+// one base, two weight tiles from another) in one block, M0 saved once.
+__device__ __forceinline__ void dma_stage5(const uint8_t* abase, uint32_t a0, uint32_t a1,
+                                           uint32_t a2, const uint8_t* bbase, uint32_t b0,
+                                           uint32_t b1, uint32_t la0, uint32_t la1, uint32_t la2,
+                                           uint32_t lb0, uint32_t lb1) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %4\n\t"
+      "s_mov_b32 m0, %9\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %4\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %4\n\t"
+      "s_mov_b32 m0, %11\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %7\n\t"
+      "s_mov_b32 m0, %12\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, %7\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(a0), "v"(a1), "v"(a2), "s"(abase), "v"(b0), "v"(b1), "s"(bbase), "s"(la0),
+        "s"(la1), "s"(la2), "s"(lb0), "s"(lb1)
       : "memory");
 }
 
@@ -160,28 +192,30 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
   if (tid == 0) hdr[0] = total;
 }
 
-// One wave's share of the DMA loads of a stage, at K-step 0; every source
-// advances by a fixed stride per K-step.  LDS offsets are relative to the
-// stage and wave-uniform.
+// One wave's share of the DMA loads of a stage.  Bases are wave-uniform and
+// at K-step 0 (each advances by a fixed stride per K-step), offsets per lane;
+// LDS offsets are relative to the stage and wave-uniform.
 struct Dma {
-  const uint8_t* a[3];  // this lane's activation chunk sources
-  const uint8_t* b[2];  // this lane's weight bytes
-  const uint8_t* s;     // this lane's scale source (4 or 16 bytes)
-  uint32_t a_lds[3], b_lds[2], s_lds;
-  int bstep;            // weight bytes per K-step
-  size_t sstep;         // scale bytes per K-step
-  int skind;            // 0: no scale load, 1: dword, 2: dwordx4 (wave-uniform)
+  const uint8_t* abase;  // activation rows
+  uint32_t aoff[3];      // this lane's chunk of row groups w, w+8, w+16
+  const uint8_t* bbase;  // the wave's first weight tile
+  uint32_t boff[2];      // this lane's 16 bytes of its two tiles
+  const uint8_t* sbase;  // scales (skind != 0)
+  uint32_t soff;
+  uint32_t la[3], lb[2], ls;
+  int bstep;             // weight bytes per K-step
+  long sstep;            // scale bytes per K-step
+  int skind;             // 0: no scale load, 1: dword, 2: dwordx4 (wave-uniform)
 };
 
 __device__ __forceinline__ void issue_stage(const Dma& d, uint32_t stage_lds, int j) {
   if (d.skind == 1)
-    dma4(d.s + (size_t)j * d.sstep, stage_lds + d.s_lds);
+    dma_x1(d.sbase + (size_t)j * d.sstep, d.soff, stage_lds + d.ls);
   else if (d.skind == 2)
-    dma16(d.s + (size_t)j * d.sstep, stage_lds + d.s_lds);
-#pragma unroll
-  for (int u = 0; u < 3; ++u) dma16(d.a[u] + (size_t)j * 128, stage_lds + d.a_lds[u]);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) dma16(d.b[u] + (size_t)j * d.bstep, stage_lds + d.b_lds[u]);
+    dma_x4(d.sbase + (size_t)j * d.sstep, d.soff, stage_lds + d.ls);
+  dma_stage5(d.abase + (size_t)j * 128, d.aoff[0], d.aoff[1], d.aoff[2],
+             d.bbase + (size_t)j * d.bstep, d.boff[0], d.boff[1], stage_lds + d.la[0],
+             stage_lds + d.la[1], stage_lds + d.la[2], stage_lds + d.lb[0], stage_lds + d.lb[1]);
 }
 
 // Operand fragments of one K-step for a wave with N live sub-tiles: its 4
@@ -202,79 +236,90 @@ struct FragsShape {
 template <int N>
 struct Head {
   uint4 b[4];
-  int sb[4];
+  uint32_t sb[2];  // up: sb[0] holds the 4 tiles' scale bytes; down: sb[u] the pair of q2-group u
   v8i a[FragsShape<N>::kHead > 0 ? FragsShape<N>::kHead : 1];
-  int sa[FragsShape<N>::kHead > 0 ? FragsShape<N>::kHead : 1];
+  uint32_t sa[FragsShape<N>::kHead > 0 ? FragsShape<N>::kHead : 1];
 };
 
 template <int N>
 struct Tail {
   v8i a[FragsShape<N>::kTail > 0 ? FragsShape<N>::kTail : 1];
-  int sa[FragsShape<N>::kTail > 0 ? FragsShape<N>::kTail : 1];
+  uint32_t sa[FragsShape<N>::kTail > 0 ? FragsShape<N>::kTail : 1];
 };
 
-__device__ __forceinline__ void read_a(v8i& a, int& sa, int lane, int row, const Stage& ca) {
-  const int g = lane >> 4;
-  const uint4 lo = *reinterpret_cast<const uint4*>(&ca.a[a_off(row, g)]);
-  const uint4 hi = *reinterpret_cast<const uint4*>(&ca.a[a_off(row, g + 4)]);
+// Per-lane LDS byte offsets (within a stage) of the wave's fragments; the
+// fragment of sub-tile i, weight tile t is at a fixed distance from them, so
+// every LDS read of a step is one base plus an immediate offset.
+struct Lds {
+  int a_lo, a_hi;  // activation row 16 wm + l%16, K chunks g and g+4 (swizzled)
+  int a_s;         // that row's scale byte of block g (a byte read: no unpacking)
+  int b;           // weight tile 0 of the wave, this lane's 16 bytes
+  int b_s;         // up: the lane's scale dword; down: its 16-bit scale pair in q2-group 2wn
+};
+
+__device__ __forceinline__ void read_a(v8i& a, uint32_t& sa, const uint8_t* S, const Lds& o, int i) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(S + o.a_lo + 4096 * i);
+  const uint4 hi = *reinterpret_cast<const uint4*>(S + o.a_hi + 4096 * i);
   a = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  sa = (int)((ca.as[row] >> (8 * g)) & 0xFFu);
+  sa = S[o.a_s + 128 * i];
 }
 
 template <bool kUp, int N>
-__device__ __forceinline__ void read_head(Head<N>& f, int lane, int wm, int wn, const Stage& c) {
-  const Stage& ca = c;
-  const Stage& cb = c;
+__device__ __forceinline__ void read_head(Head<N>& f, const uint8_t* S, const Lds& o) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    f.b[t] = *reinterpret_cast<const uint4*>(S + o.b + (kUp ? 1024 * t : 2048 * (t >> 1) + 1024 * (t & 1)));
   if (kUp) {
-    const uint32_t w = cb.bs[wn * 64 + lane];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f.sb[t] = (int)((w >> (8 * t)) & 0xFFu);
-      f.b[t] = *reinterpret_cast<const uint4*>(&cb.b[wn * 4096 + t * 1024 + lane * 16]);
-    }
+    f.sb[0] = *reinterpret_cast<const uint32_t*>(S + o.b_s);
   } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int g2 = 2 * wn + (t >> 1);
-      f.sb[t] = (int)((cb.bs[g2 * 32 + (lane >> 1)] >> (16 * (lane & 1) + 8 * (t & 1))) & 0xFFu);
-      f.b[t] = *reinterpret_cast<const uint4*>(&cb.b[g2 * 2048 + (t & 1) * 1024 + lane * 16]);
-    }
+    f.sb[0] = *reinterpret_cast<const uint16_t*>(S + o.b_s);
+    f.sb[1] = *reinterpret_cast<const uint16_t*>(S + o.b_s + 128);
   }
 #pragma unroll
-  for (int i = 0; i < FragsShape<N>::kHead; ++i)
-    read_a(f.a[i], f.sa[i], lane, 16 * (wm + 2 * i) + (lane & 15), ca);
+  for (int i = 0; i < FragsShape<N>::kHead; ++i) read_a(f.a[i], f.sa[i], S, o, i);
 }
 
 template <int N>
-__device__ __forceinline__ void read_tail(Tail<N>& f, int lane, int wm, const Stage& ca) {
+__device__ __forceinline__ void read_tail(Tail<N>& f, const uint8_t* S, const Lds& o) {
 #pragma unroll
   for (int i = 0; i < FragsShape<N>::kTail; ++i)
-    read_a(f.a[i], f.sa[i], lane, 16 * (wm + 2 * (FragsShape<N>::kHead + i)) + (lane & 15), ca);
+    read_a(f.a[i], f.sa[i], S, o, FragsShape<N>::kHead + i);
 }
 
-template <int N>
+// Weight tile t's scale: byte t of the up dword, byte t&1 of the down pair
+// of q2-group t>>1 -- selected by the MFMA's scale operand byte select.
+template <bool kUp, int T>
+__device__ __forceinline__ v4f mfma_t(v8i a, uint32_t sa, uint4 b, const uint32_t* sb, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, widen_fp4(b), c, 0, 4, 0, (int)sa,
+                                                          kUp ? T : (T & 1),
+                                                          (int)(kUp ? sb[0] : sb[T >> 1]));
+}
+
+template <bool kUp, int N>
+__device__ __forceinline__ void mfma_row(v8i a, uint32_t sa, const Head<N>& h, v4f (&acc)[4]) {
+  acc[0] = mfma_t<kUp, 0>(a, sa, h.b[0], h.sb, acc[0]);
+  acc[1] = mfma_t<kUp, 1>(a, sa, h.b[1], h.sb, acc[1]);
+  acc[2] = mfma_t<kUp, 2>(a, sa, h.b[2], h.sb, acc[2]);
+  acc[3] = mfma_t<kUp, 3>(a, sa, h.b[3], h.sb, acc[3]);
+}
+
+template <bool kUp, int N>
 __device__ __forceinline__ void mfma_head(const Head<N>& f, v4f (&acc)[N][4]) {
 #pragma unroll
-  for (int i = 0; i < FragsShape<N>::kHead; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      acc[i][t] = mfma_fp8_fp4(f.a[i], widen_fp4(f.b[t]), acc[i][t], f.sa[i], f.sb[t]);
+  for (int i = 0; i < FragsShape<N>::kHead; ++i) mfma_row<kUp, N>(f.a[i], f.sa[i], f, acc[i]);
 }
 
-template <int N>
+template <bool kUp, int N>
 __device__ __forceinline__ void mfma_tail(const Head<N>& h, const Tail<N>& f, v4f (&acc)[N][4]) {
 #pragma unroll
   for (int i = 0; i < FragsShape<N>::kTail; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      v4f& c = acc[FragsShape<N>::kHead + i][t];
-      c = mfma_fp8_fp4(f.a[i], widen_fp4(h.b[t]), c, f.sa[i], h.sb[t]);
-    }
+    mfma_row<kUp, N>(f.a[i], f.sa[i], h, acc[FragsShape<N>::kHead + i]);
 }
 
 template <bool kUp, int N>
-__device__ __forceinline__ void gemm_body(const Dma& d, Stage* st, int J, int lane, int wm, int wn,
-                                          int rows, int m0, int ft, int I, int H, int QG2,
+__device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st, int J, int lane,
+                                          int wm, int wn, int rows, int m0, int ft, int I, int H,
+                                          int QG2,
                                           uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
                                           float* __restrict__ O) {
   v4f acc[N > 0 ? N : 1][4];
@@ -296,13 +341,15 @@ __device__ __forceinline__ void gemm_body(const Dma& d, Stage* st, int J, int la
   // j + 3.
   auto step = [&](int j, Head<N>& hc, Head<N>& hn) {
     Tail<N> tl;
-    if constexpr (N > 0) read_tail<N>(tl, lane, wm, st[j % kRing]);
-    if constexpr (N > 0) mfma_head<N>(hc, acc);
+    const uint8_t* Sc = reinterpret_cast<const uint8_t*>(&st[j % kRing]);
+    const uint8_t* Sn = reinterpret_cast<const uint8_t*>(&st[(j + 1) % kRing]);
+    if constexpr (N > 0) read_tail<N>(tl, Sc, o);
+    if constexpr (N > 0) mfma_head<kUp, N>(hc, acc);
     wait_vmcnt<kOps>();
     __syncthreads();
-    if constexpr (N > 0) read_head<kUp, N>(hn, lane, wm, wn, st[(j + 1) % kRing]);
+    if constexpr (N > 0) read_head<kUp, N>(hn, Sn, o);
     issue(j + kRing);
-    if constexpr (N > 0) mfma_tail<N>(hc, tl, acc);
+    if constexpr (N > 0) mfma_tail<kUp, N>(hc, tl, acc);
   };
   issue(0);
   issue(1);
@@ -310,7 +357,7 @@ __device__ __forceinline__ void gemm_body(const Dma& d, Stage* st, int J, int la
   Head<N> h0, h1;
   wait_vmcnt<2 * kOps>();
   __syncthreads();
-  if constexpr (N > 0) read_head<kUp, N>(h0, lane, wm, wn, st[0]);
+  if constexpr (N > 0) read_head<kUp, N>(h0, reinterpret_cast<const uint8_t*>(&st[0]), o);
   int j = 0;
   if (J & 1) {  // odd J: one step first, so the loop below takes steps in pairs
     step(0, h0, h1);
@@ -413,30 +460,31 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
   // Activations: row group rg = wave + 8u (u < 3) holds rows 8rg..8rg+7,
   // 1 KiB at stage offset 1024 rg; lane l lands at row 8rg + l/8, physical
   // chunk l%8, which holds logical chunk (l%8) ^ (l/8) (the row's low 3 bits
-  // are l/8).
+  // are l/8).  Offsets are from the activation base (token rows for gate/up,
+  // the tile's first sorted row for down).
+  d.abase = kUp ? act : act + (size_t)m0 * K;
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
     const int rg = wave + 8 * u;
     const int r = 8 * rg + (lane >> 3);
     const int src = row_src[r] >= 0 ? row_src[r] : row0;
-    d.a[u] = act + (size_t)src * K + (((lane & 7) ^ (lane >> 3)) << 4);
-    d.a_lds[u] = (uint32_t)(1024 * rg);
+    d.aoff[u] = (uint32_t)((kUp ? (size_t)src : (size_t)(src - m0)) * K) + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+    d.la[u] = (uint32_t)(1024 * rg);
   }
-  // Weights: stage tiles 2w, 2w+1 (1 KiB each, lane order = packed order).
-  // up: tile index 4g + t = q-group 4ft + g, tile t; down: tile index
-  // 2g2 + t = q2-group 8ft + g2, tile t (groups past H read group 0, whose
-  // products are never stored).
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ti = 2 * wave + u;
-    if (kUp) {
-      d.b[u] = packed + L.upw_block(e, 4 * ft + (ti >> 2), 0) + (ti & 3) * 1024 + lane * 16;
-    } else {
-      const int g2 = 8 * ft + (ti >> 1);
-      d.b[u] = packed + L.dnw_block(e, g2 < QG2 ? g2 : 0, 0) + (ti & 1) * 1024 + lane * 16;
-    }
-    d.b_lds[u] = (uint32_t)(kABytes + 1024 * ti);
+  // Weights: stage tiles 2w, 2w+1 (1 KiB each, lane order = packed order),
+  // adjacent in the packed layout.  up: tile index 4g + t = q-group 4ft + g,
+  // tile t; down: tile index 2g2 + t = q2-group 8ft + g2, tile t (groups past
+  // H read group 0, whose products are never stored).
+  if (kUp) {
+    d.bbase = packed + L.upw_block(e, 4 * ft + (wave >> 1), 0) + (size_t)(2 * (wave & 1)) * 1024;
+  } else {
+    const int g2 = 8 * ft + wave;
+    d.bbase = packed + L.dnw_block(e, g2 < QG2 ? g2 : 0, 0);
   }
+  d.boff[0] = (uint32_t)(lane * 16);
+  d.boff[1] = (uint32_t)(lane * 16 + 1024);
+  d.lb[0] = (uint32_t)(kABytes + 2048 * wave);
+  d.lb[1] = (uint32_t)(kABytes + 2048 * wave + 1024);
   d.bstep = kUp ? 4096 : 2048;
   // Scales.  Waves 0-2: activation scale dwords of rows 64w..64w+63 (as[row])
   // from the by-step array, one contiguous run per K-step (rows past the
@@ -445,27 +493,46 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
   // 4ft + g's 256 bytes (bs[64g + d]); down: lanes 8g2..8g2+7 take q2-group
   // 8ft + g2's 128 bytes (bs[32 g2 + d]).
   if (wave < 3) {
-    const int r = 64 * wave + lane;
-    d.s = reinterpret_cast<const uint8_t*>(sT + m0 + min(r, rows - 1));
-    d.sstep = (size_t)P * 4;
-    d.s_lds = (uint32_t)(kABytes + kBBytes + 256 * wave);
+    d.sbase = reinterpret_cast<const uint8_t*>(sT + m0);
+    d.soff = (uint32_t)(min(64 * wave + lane, rows - 1) * 4);
+    d.sstep = P * 4;
+    d.ls = (uint32_t)(kABytes + kBBytes + 256 * wave);
     d.skind = 1;
   } else if (wave == 3) {
     if (kUp) {
-      d.s = packed + L.ups_block(e, 4 * ft + (lane >> 4), 0) + (lane & 15) * 16;
+      d.sbase = packed + L.ups_block(e, 4 * ft, 0);
+      d.soff = (uint32_t)((lane >> 4) * L.J * 256 + (lane & 15) * 16);
       d.sstep = 256;
     } else {
       const int g2 = 8 * ft + (lane >> 3);
-      d.s = packed + L.dns_block(e, g2 < QG2 ? g2 : 0, 0) + (lane & 7) * 16;
+      d.sbase = packed + L.dns_block(e, 8 * ft, 0);
+      d.soff = (uint32_t)((g2 < QG2 ? (lane >> 3) : 0) * L.J2 * 128 + (lane & 7) * 16);
       d.sstep = 128;
     }
-    d.s_lds = (uint32_t)(kABytes + kBBytes + kBM * 4);
+    d.ls = (uint32_t)(kABytes + kBBytes + kBM * 4);
     d.skind = 2;
   } else {
-    d.s = nullptr;
+    d.sbase = nullptr;
+    d.soff = 0;
     d.sstep = 0;
-    d.s_lds = 0;
+    d.ls = 0;
     d.skind = 0;
+  }
+  // LDS read offsets of this lane's fragments (see Lds)
+  Lds o;
+  {
+    const int l15 = lane & 15, g = lane >> 4;
+    const int row = 16 * wm + l15;
+    o.a_lo = row * 128 + ((g ^ (l15 & 7)) << 4);
+    o.a_hi = row * 128 + (((g + 4) ^ (l15 & 7)) << 4);
+    o.a_s = kABytes + kBBytes + row * 4 + g;
+    if (kUp) {
+      o.b = kABytes + wn * 4096 + lane * 16;
+      o.b_s = kABytes + kBBytes + kBM * 4 + (wn * 64 + lane) * 4;
+    } else {
+      o.b = kABytes + 2 * wn * 2048 + lane * 16;
+      o.b_s = kABytes + kBBytes + kBM * 4 + (2 * wn * 32 + (lane >> 1)) * 4 + 2 * (lane & 1);
+    }
   }
 
   const int J = K / 128;
@@ -476,13 +543,13 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
     if (wm + 2 * i < nsub) nact = i + 1;
   nact = __builtin_amdgcn_readfirstlane(nact);
   switch (nact) {
-    case 0: gemm_body<kUp, 0>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 1: gemm_body<kUp, 1>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 2: gemm_body<kUp, 2>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 3: gemm_body<kUp, 3>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 4: gemm_body<kUp, 4>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 5: gemm_body<kUp, 5>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    default: gemm_body<kUp, 6>(d, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 0: gemm_body<kUp, 0>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 1: gemm_body<kUp, 1>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 2: gemm_body<kUp, 2>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 3: gemm_body<kUp, 3>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 4: gemm_body<kUp, 4>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    case 5: gemm_body<kUp, 5>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    default: gemm_body<kUp, 6>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
   }
 }
 
