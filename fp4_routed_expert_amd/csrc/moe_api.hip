@@ -214,6 +214,8 @@ moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, co
   if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   const PackedLayout L(w->E, w->H, w->I);
   const uint8_t* pk = static_cast<const uint8_t*>(w->packed);
+  // the prefill kernel addresses activation rows with 32-bit offsets
+  if (path == 1 && (int64_t)T * w->H >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   if (path == 1)
     return hip_status(launch_up_prefill(pk, L, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs,
                                         workspace, stream));

@@ -117,6 +117,9 @@ def test_forward_argument_errors():
     assert sws >= 32 * (256 // 128) * 4          # the activation scales by K-step
     assert L.moe_fp4_stage_workspace_size(16, 2, 8, 200, 128) == 0
     assert up(ctypes.byref(d), A, A, A, A, 16, 2, A, A, A, sws - 1, 0, NUL) == WSE
+    big = _desc(E=8, H=1 << 20, I=128)
+    bws = L.moe_fp4_stage_workspace_size(4096, 2, 8, 1 << 20, 128)
+    assert up(ctypes.byref(big), A, A, A, A, 4096, 2, A, A, A, bws, 2, NUL) == UNS  # T*H >= 2^32, prefill
     assert L.moe_combine(A, A, A, 4, 2, 250, A, NUL) == UNS       # H % 4
     assert L.moe_combine(A, A, A, 4, 0, 256, A, NUL) == INV
 
