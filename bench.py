@@ -77,6 +77,98 @@ def rocprof_summary(paths) -> str:
     return "\n".join(out)
 
 
+KERNEL_SOURCES = {
+    "up_decode_kernel": "fp4_routed_expert_amd/csrc/expert_decode.hip",
+    "prefill_gemm_kernel<true>": "fp4_routed_expert_amd/csrc/expert_prefill.hip",
+}
+
+
+def source_sha256(kernel: str) -> str:
+    import hashlib
+    return hashlib.sha256(open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb").read()).hexdigest()
+
+
+def _counter_means(path: str, counter: str):
+    """Per-kernel list of per-dispatch values of one counter from a rocprofv3 CSV directory."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+            name = name.replace("void ", "")
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, kernel: str, workload: str, cfg: str = "c1",
+                    steps: int = 20) -> str:
+    """HBM traffic per launch of `kernel` from a FETCH_SIZE run and a WRITE_SIZE run,
+    each counter scaled so that the 1 GiB device copies of --copy-calibration
+    read and write exactly 1 GiB."""
+    f = _counter_means(fetch_dir, "FETCH_SIZE")
+    w = _counter_means(write_dir, "WRITE_SIZE")
+    copy = [k for k in f if "copyBuffer" in k]
+    if not copy or kernel not in f or kernel not in w:
+        raise SystemExit(f"missing kernels in counter runs: have {sorted(f)}")
+    cf = sorted(f[copy[0]])[-20:]   # the calibration copies are the largest copy dispatches
+    cw = sorted(w[copy[0]])[-20:]
+    gib_kib = float(1 << 20)
+    fetch_scale = gib_kib / (sum(cf) / len(cf))
+    write_scale = gib_kib / (sum(cw) / len(cw))
+    kf = sum(f[kernel]) / len(f[kernel])
+    kw = sum(w[kernel]) / len(w[kernel])
+    traffic = (kf * fetch_scale + kw * write_scale) * 1024.0
+    lines = [
+        f"# HBM traffic: {kernel}, {workload}",
+        "",
+        "Commands (repo root, one MI355X; each counter in its own run):",
+        "",
+        "```",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o f -- python3 bench.py "
+        f"--config {cfg} --steps {steps} --warmup 2 --cpu-budget 0 --copy-calibration",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o w -- python3 bench.py "
+        f"--config {cfg} --steps {steps} --warmup 2 --cpu-budget 0 --copy-calibration",
+        f"python3 bench.py --traffic-summary {fetch_dir} {write_dir} --kernel '{kernel}' "
+        f"--workload '{workload}' --config {cfg} --steps {steps}",
+        "```",
+        "",
+        "The 1 GiB copies of --copy-calibration run in the same process; FETCH_SIZE reads half",
+        "of the bytes a copy moves, so it is scaled by the factor below.",
+        "",
+        f"- dispatches: {len(f[kernel])} (FETCH_SIZE run), {len(w[kernel])} (WRITE_SIZE run)",
+        f"- FETCH_SIZE per dispatch: {kf:.1f} KiB (raw)",
+        f"- WRITE_SIZE per dispatch: {kw:.1f} KiB (raw)",
+        f"- calibration: 1 GiB device copy reads as FETCH_SIZE {sum(cf) / len(cf):.1f} KiB, "
+        f"WRITE_SIZE {sum(cw) / len(cw):.1f} KiB; scale factors {fetch_scale:.4f} / {write_scale:.4f}",
+        f"- source_sha256: {source_sha256(kernel)}",
+        f"- traffic_bytes_per_launch: {traffic:.0f}",
+        "",
+    ]
+    return "\n".join(lines)
+
+
+def load_traffic(kernel: str, workload: str):
+    """traffic_bytes_per_launch from the committed summary, if it was taken on
+    the kernel source as it is now (else None)."""
+    import glob
+    for f in glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md")):
+        text = open(f).read()
+        if f"# HBM traffic: {kernel}, {workload}" not in text:
+            continue
+        sha = traffic = None
+        for line in text.splitlines():
+            if line.startswith("- source_sha256: "):
+                sha = line.split(": ", 1)[1].strip()
+            if line.startswith("- traffic_bytes_per_launch: "):
+                traffic = float(line.split(": ", 1)[1])
+        if sha == source_sha256(kernel) and traffic is not None:
+            return traffic
+    return None
+
+
 def copy_calibration(reps: int = 20):
     """A plain device copy of 1 GiB, `reps` times: 1 GiB read + 1 GiB written per
     dispatch, the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -121,9 +213,17 @@ def main():
                     help="also run 20 plain 1 GiB device copies (HBM counter calibration)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="PATH",
                     help="print a markdown summary of rocprofv3 CSV outputs and exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM traffic summary of --kernel from two counter runs and exit")
+    ap.add_argument("--kernel", default="up_decode_kernel")
+    ap.add_argument("--workload", default="")
     args = ap.parse_args()
     if args.rocprof_summary:
         print(rocprof_summary(args.rocprof_summary))
+        return
+    if args.traffic_summary:
+        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.kernel, args.workload,
+                              args.config, args.steps))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -211,14 +311,18 @@ def main():
     prefill = args.flags == 2 or (args.flags == 0 and P > 16 * E)
     if prefill:
         achieved = up_flops / (up_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "up_prefill_kernel (gate/up GEMM + SwiGLU + MXFP8)",
+        kname = "prefill_gemm_kernel<true>"
+        roof = {"bound": "mfma", "kernel": kname + " (gate/up GEMM + SwiGLU + MXFP8 of h)",
                 "achieved": achieved, "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_FP8_PEAK_TFLOPS, "traffic": None,
+                "frac": achieved / MFMA_FP8_PEAK_TFLOPS,
+                "traffic": load_traffic(kname, synth.CONFIG_NAMES.get(args.config, args.config)),
                 "alg_flops_per_launch": up_flops, "avg_launch_us": up_ms * 1e3}
     else:
-        roof = {"bound": "hbm", "kernel": "up_decode_kernel (gate/up GEMM + SwiGLU + MXFP8)",
+        kname = "up_decode_kernel"
+        roof = {"bound": "hbm", "kernel": kname + " (gate/up GEMM + SwiGLU + MXFP8 of h)",
                 "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": up_gbs / HBM_PEAK_GBS, "traffic": None,
+                "frac": up_gbs / HBM_PEAK_GBS,
+                "traffic": load_traffic(kname, synth.CONFIG_NAMES.get(args.config, args.config)),
                 "alg_bytes_per_launch": b_up, "avg_launch_us": up_ms * 1e3}
     line = {
         "metric": METRIC,
