@@ -27,24 +27,53 @@ __device__ __forceinline__ uint32_t mx_scale_from_amax(float amax, float* mul) {
 }
 
 // Round an fp32 value (|a| < 512 after scaling) to an OCP e4m3fn code:
-// nearest, ties to even, saturating at 448, sign kept.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float a) {
-  const uint32_t u = __float_as_uint(a);
+// nearest, ties to even, saturating at 448, sign kept.  The three ranges are
+// all computed and one selected, so the conversion has no branches.
+__host__ __device__ __forceinline__ uint32_t f32_to_e4m3(float a) {
+  uint32_t u;
+  __builtin_memcpy(&u, &a, 4);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t mag = u & 0x7FFFFFFFu;
-  if (mag >= 0x43E00000u) return sign | 0x7Eu;             // >= 448
-  if (mag < 0x3C800000u) {                                  // < 2^-6: steps of 2^-9
-    const float m = __uint_as_float(mag) * 512.0f;          // exact
-    return sign | (uint32_t)__builtin_rintf(m);             // 0..8 (8 = 2^-6)
-  }
-  // keep 3 of the 23 mantissa bits, round to nearest even on the bit pattern;
-  // a carry moves into the exponent field, which is the correct next binade
-  const uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);
-  return sign | ((r >> 20) - (120u << 3));                  // rebias 127 -> 7
+  // below 2^-6 the codes step by 2^-9: round |a| * 512 (exact) to an integer 0..8
+  const uint32_t mag_sub = (mag < 0x3C800000u) ? mag : 0u;  // other ranges: a dummy 0
+  float m;
+  __builtin_memcpy(&m, &mag_sub, 4);
+  const uint32_t sub = (uint32_t)(int)__builtin_rintf(m * 512.0f);
+  // normal: keep 3 of the 23 mantissa bits, round to nearest even on the bit
+  // pattern; a carry moves into the exponent field, which is the correct next
+  // binade; then rebias 127 -> 7
+  const uint32_t nrm = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
+  uint32_t c = (mag < 0x3C800000u) ? sub : nrm;
+  c = (mag >= 0x43E00000u) ? 0x7Eu : c;  // >= 448
+  return sign | c;
 }
 
+// SiLU(g) * u with the hardware exponential and reciprocal (fp32, about one
+// ulp each): the result is rounded to fp8 right after.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// One DPP lane permutation (no LDS traffic); every source lane is inside the
+// destination's row of 16, so no lane reads outside the wave.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Maximum over each quad of 4 lanes, returned to every lane of the quad.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));  // quad_perm [1,0,3,2]
+  return fmaxf(v, dpp_f32<0x4E>(v));  // quad_perm [2,3,0,1]
+}
+
+// Maximum over each row of 16 lanes, returned to every lane of the row: the
+// quad maximum, then the half-row mirror (lane i <-> 7-i of each 8) joins the
+// two quads of a half and the row mirror (i <-> 15-i) the two halves.
+__device__ __forceinline__ float row16_max(float v) {
+  v = quad_max(v);
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
 }
 
 // ------------------------------------------------------------------ scans

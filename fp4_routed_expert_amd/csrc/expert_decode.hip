@@ -194,9 +194,7 @@ __global__ __launch_bounds__(kUpNW * 64) void up_decode_kernel(
       for (int v = 0; v < 4; ++v) {
         const float h0 = silu_mul(s[0][v], s[2][v]);
         const float h1 = silu_mul(s[1][v], s[3][v]);
-        float am = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
+        const float am = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
         float mul;
         const uint32_t sc = mx_scale_from_amax(am, &mul);
         const int r = m0 + 4 * (lane >> 4) + v;

@@ -381,9 +381,7 @@ __device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st,
       for (int v = 0; v < 4; ++v) {
         const float h0 = silu_mul(acc[i][0][v], acc[i][2][v]);
         const float h1 = silu_mul(acc[i][1][v], acc[i][3][v]);
-        float am = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
+        const float am = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
         float mul;
         const uint32_t sc = mx_scale_from_amax(am, &mul);
         const int r = rbase + v;

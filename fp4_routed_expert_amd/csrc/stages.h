@@ -169,7 +169,7 @@ __device__ void sort_small_body(const int32_t* ids, int P, int E, SortSmallLds& 
 // ------------------------------------------------------------------- MXFP8
 // One lane's share of the MXFP8 quantisation of bf16 data: the 8-element
 // group i (one 128-bit load); four consecutive lanes hold one 32-element block
-// and reduce its maximum with two xor shuffles, so all 64 lanes of the wave
+// and reduce its maximum with two DPP quad swaps, so all 64 lanes of the wave
 // must call this together.  Writes 8 codes as one 64-bit store and, on the
 // block's first lane, the E8M0 scale.
 __device__ __forceinline__ void quant_group8(const uint4* __restrict__ x, long i, long n8,
@@ -186,8 +186,7 @@ __device__ __forceinline__ void quant_group8(const uint4* __restrict__ x, long i
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = quad_max(amax);
   float mul;
   const uint32_t scode = mx_scale_from_amax(amax, &mul);
   uint32_t lo = 0, hi = 0;
