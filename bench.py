@@ -261,7 +261,7 @@ def main():
     xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
     hq = torch.empty((P, I), dtype=torch.uint8, device=dev)
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=dev)
-    O = torch.empty((P, H), dtype=torch.float32, device=dev)
+    O = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, k, E, H, I), 256),
                            dtype=torch.uint8, device=dev)

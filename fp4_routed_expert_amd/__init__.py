@@ -164,10 +164,11 @@ def expert_up(pw: PackedWeights, xq, xs, offsets, sorted_pair, T: int, k: int, f
 
 def expert_down(pw: PackedWeights, hq, hs, offsets, T: int, k: int, flags: int = 0, O=None,
                 workspace=None):
-    """Down GEMM -> O [T*k, H] fp32, sorted order."""
+    """Down GEMM -> O [T*k, H] bf16 (fp32 accumulation, rounded once), sorted order."""
     dev = hq.device
     if O is None:
-        O = torch.empty((T * k, pw.H), dtype=torch.float32, device=dev)
+        O = torch.empty((T * k, pw.H), dtype=torch.bfloat16, device=dev)
+    _check_dtype(O, (torch.bfloat16,), "O")
     workspace = _stage_ws(T, k, pw, dev, workspace)
     _lib.check(_lib.lib().moe_fp4_expert_down(
         ctypes.byref(pw.desc), _ptr(hq), _ptr(hs), _ptr(offsets), T, k, _ptr(O), _ptr(workspace),
@@ -176,6 +177,8 @@ def expert_down(pw: PackedWeights, hq, hs, offsets, T: int, k: int, flags: int =
 
 
 def combine(O, gates, pair_pos, T: int, k: int, H: int, y=None):
+    """y [T, H] fp32 = gate-weighted sum of the bf16 expert outputs O, in slot order."""
+    _check_dtype(O, (torch.bfloat16,), "O")
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=O.device)
     _lib.check(_lib.lib().moe_combine(_ptr(O), _ptr(gates), _ptr(pair_pos), T, k, H, _ptr(y),

@@ -48,6 +48,12 @@ __host__ __device__ __forceinline__ uint32_t f32_to_e4m3(float a) {
   return sign | c;
 }
 
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 // SiLU(g) * u with the hardware exponential and reciprocal (fp32, about one
 // ulp each): the result is rounded to fp8 right after.
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -193,7 +199,7 @@ hipError_t launch_up_decode(const uint8_t* packed, const PackedLayout& L, const 
                             const int32_t* sorted_pair, int k, uint8_t* hq, uint8_t* hs,
                             hipStream_t s);
 hipError_t launch_down_decode(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
-                              const uint8_t* hs, const int32_t* offsets, float* O,
+                              const uint8_t* hs, const int32_t* offsets, uint16_t* O,
                               hipStream_t s);
 size_t prefill_stage_bytes(long P, int E, int H, int I);
 hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
@@ -201,9 +207,9 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
                              const int32_t* sorted_pair, int T, int k, uint8_t* hq, uint8_t* hs,
                              void* tile_ws, hipStream_t s);
 hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
-                               const uint8_t* hs, const int32_t* offsets, int T, int k, float* O,
+                               const uint8_t* hs, const int32_t* offsets, int T, int k, uint16_t* O,
                                void* tile_ws, hipStream_t s);
-hipError_t launch_combine(const float* O, const float* gates, const int32_t* pair_pos, int T,
+hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos, int T,
                           int k, int H, float* y, hipStream_t s);
 
 }  // namespace moe

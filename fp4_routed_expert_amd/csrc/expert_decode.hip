@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kUpNW * 64) void up_decode_kernel(
 
 __global__ __launch_bounds__(kDnNW * 64) void down_decode_kernel(
     const uint8_t* __restrict__ packed, PackedLayout L, const uint8_t* __restrict__ hq,
-    const uint8_t* __restrict__ hs, const int32_t* __restrict__ offsets, float* __restrict__ O) {
+    const uint8_t* __restrict__ hs, const int32_t* __restrict__ offsets, uint16_t* __restrict__ O) {
   const int QT2 = L.H / 32;
   const int e = blockIdx.x / QT2, q2 = blockIdx.x % QT2;
   const int seg0 = offsets[e], seg1 = offsets[e + 1];
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kDnNW * 64) void down_decode_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = m0 + 4 * (lane >> 4) + v;
-          if (r < seg1) O[(size_t)r * H + q2 * 32 + t * 16 + (lane & 15)] = s[v];
+          if (r < seg1) O[(size_t)r * H + q2 * 32 + t * 16 + (lane & 15)] = f32_to_bf16(s[v]);
         }
       }
     }
@@ -266,7 +266,7 @@ hipError_t launch_up_decode(const uint8_t* packed, const PackedLayout& L, const 
 }
 
 hipError_t launch_down_decode(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
-                              const uint8_t* hs, const int32_t* offsets, float* O,
+                              const uint8_t* hs, const int32_t* offsets, uint16_t* O,
                               hipStream_t s) {
   const unsigned grid = (unsigned)L.E * (unsigned)(L.H / 32);
   hipLaunchKernelGGL(down_decode_kernel, dim3(grid), dim3(kDnNW * 64), 0, s, packed, L, hq, hs,

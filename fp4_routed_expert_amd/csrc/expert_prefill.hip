@@ -321,7 +321,7 @@ __device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st,
                                           int wm, int wn, int rows, int m0, int ft, int I, int H,
                                           int QG2,
                                           uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
-                                          float* __restrict__ O) {
+                                          uint16_t* __restrict__ O) {
   v4f acc[N > 0 ? N : 1][4];
 #pragma unroll
   for (int i = 0; i < N; ++i)
@@ -401,7 +401,7 @@ __device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st,
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = rbase + v;
-          if (r < rows) O[(size_t)(m0 + r) * H + col] = acc[i][t][v];
+          if (r < rows) O[(size_t)(m0 + r) * H + col] = f32_to_bf16(acc[i][t][v]);
         }
       }
     }
@@ -425,13 +425,13 @@ __global__ __launch_bounds__(256) void scales_by_step_kernel(const uint32_t* __r
 
 // kUp: gate/up GEMM (A = x rows gathered by token, K = H; B = W1/W3; epilogue
 // SwiGLU + MXFP8 of h).  !kUp: down GEMM (A = h rows in sorted order, K = I;
-// B = W2; epilogue fp32 store of O).
+// B = W2; epilogue bf16 store of O).
 template <bool kUp>
 __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
     const uint8_t* __restrict__ packed, PackedLayout L, const uint8_t* __restrict__ act,
     const uint32_t* __restrict__ sT, long P, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pair, int k, const int* __restrict__ hdr, int NF,
-    int nblocks, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, float* __restrict__ O) {
+    int nblocks, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ O) {
   __shared__ __align__(16) Stage st[kRing];
   __shared__ int row_src[kBM];
   const int logical = xcd_work_item(blockIdx.x, hdr[0] * NF);
@@ -578,12 +578,12 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
   const int NF = L.I / 128;
   const long nb = (max_tiles(P, L.E) * NF + 7) / 8 * 8;
   hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)nb), dim3(kThreads), 0, s, packed, L,
-                     xq, sT, P, offsets, sorted_pair, k, hdr, NF, (int)nb, hq, hs, (float*)nullptr);
+                     xq, sT, P, offsets, sorted_pair, k, hdr, NF, (int)nb, hq, hs, (uint16_t*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
-                               const uint8_t* hs, const int32_t* offsets, int T, int k, float* O,
+                               const uint8_t* hs, const int32_t* offsets, int T, int k, uint16_t* O,
                                void* tile_ws, hipStream_t s) {
   const long P = (long)T * k;
   int* hdr = static_cast<int*>(tile_ws);

@@ -74,7 +74,7 @@ FwdCarve carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
   c.hq = 0;
   c.hs = align256(c.hq + P * I);
   c.O = align256(c.hs + P * (I / 32));
-  c.stage = align256(c.O + P * H * sizeof(float));
+  c.stage = align256(c.O + P * H * sizeof(uint16_t));
   c.total = align256(c.stage + stage_ws_bytes(T, k, E, H, I));
   return c;
 }
@@ -223,7 +223,7 @@ moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, co
 }
 
 moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, const uint8_t* hs,
-                                 const int32_t* expert_offsets, int32_t T, int32_t k, float* O,
+                                 const int32_t* expert_offsets, int32_t T, int32_t k, uint16_t* O,
                                  void* workspace, size_t workspace_bytes, uint32_t flags,
                                  hipStream_t stream) {
   moe_status_t st = check_weights(w);
@@ -244,13 +244,13 @@ moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, 
   return hip_status(launch_down_decode(pk, L, hq, hs, expert_offsets, O, stream));
 }
 
-moe_status_t moe_combine(const float* O, const float* topk_gates, const int32_t* pair_pos,
+moe_status_t moe_combine(const uint16_t* O, const float* topk_gates, const int32_t* pair_pos,
                          int32_t T, int32_t k, int32_t H, float* y, hipStream_t stream) {
   if (T < 0 || k < 1 || H < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (k > kMaxK || H % 4 != 0) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!O || !topk_gates || !pair_pos || !y) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(O, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(O, 8) || !aligned(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
   return hip_status(launch_combine(O, topk_gates, pair_pos, T, k, H, y, stream));
 }
 
@@ -282,7 +282,7 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w, const uint8_t* 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* hq = ws + c.hq;
   uint8_t* hs = ws + c.hs;
-  float* O = reinterpret_cast<float*>(ws + c.O);
+  uint16_t* O = reinterpret_cast<uint16_t*>(ws + c.O);
   void* stage = ws + c.stage;
   const size_t stage_bytes = c.total - c.stage;
   st = moe_fp4_expert_up(w, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs, stage,

@@ -171,24 +171,27 @@ moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w /*(host)*/,
                                uint32_t flags, hipStream_t stream);
 
 /*
- * Expert down GEMM (step 6): O[s,r] = sum_i h[s,i] W2[e,r,i], fp32, rows in
- * sorted order.
+ * Expert down GEMM (step 6): O[s,r] = sum_i h[s,i] W2[e,r,i], rows in sorted
+ * order, accumulated in fp32 and stored as bf16 (round to nearest even): a
+ * matrix-multiply output kept at low precision, its sum over experts taken
+ * in fp32 by moe_combine (pwwt.cn review, section 4.1, the precision table).
  *   hq [T*k, I], hs [T*k, I/32] from moe_fp4_expert_up
- *   O  [T*k, H] fp32 (out)
+ *   O  [T*k, H] bf16 bits (out, 16-byte aligned)
  */
 moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w /*(host)*/,
                                  const uint8_t* hq, const uint8_t* hs,
                                  const int32_t* expert_offsets, int32_t T, int32_t k,
-                                 float* O, void* workspace, size_t workspace_bytes,
+                                 uint16_t* O, void* workspace, size_t workspace_bytes,
                                  uint32_t flags, hipStream_t stream);
 
 /*
  * Gate-weighted combine (step 7): y[t,r] = sum_{j=0..k-1, in this order}
- * gates[t,j] * O[pair_pos[t*k+j], r], fp32, no atomics.
- *   O [T*k, H] fp32; topk_gates [T, k]; pair_pos [T*k]; y [T, H] fp32 (out)
+ * gates[t,j] * O[pair_pos[t*k+j], r], fp32 fused multiply-adds, no atomics.
+ *   O [T*k, H] bf16 bits (8-byte aligned); topk_gates [T, k]; pair_pos [T*k];
+ *   y [T, H] fp32 (out, 16-byte aligned)
  *   H % 4 == 0
  */
-moe_status_t moe_combine(const float* O, const float* topk_gates, const int32_t* pair_pos,
+moe_status_t moe_combine(const uint16_t* O, const float* topk_gates, const int32_t* pair_pos,
                          int32_t T, int32_t k, int32_t H, float* y, hipStream_t stream);
 
 /*
