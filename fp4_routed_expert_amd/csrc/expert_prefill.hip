@@ -8,20 +8,22 @@
 // block scales applied by the instruction, FP8 issue rate).
 //
 // Work list: a small kernel turns the expert offsets into a list of token tiles
-// (expert, first sorted row) of up to kBM rows, on the device, so the grid is
-// sized from host-known bounds only (sum_e ceil(n_e/kBM) <= ceil(P/kBM) + E)
-// and no count is ever read back to the host; workgroups past the tile count
-// exit.  kBM = 192 covers a whole expert at the prefill shape (113-180 rows
+// (expert, first sorted row) of up to kBM rows, on the device; no count is
+// ever read back to the host.  A work item is a (token tile, feature tile)
+// pair.  kBM = 192 covers a whole expert at the prefill shape (113-180 rows
 // per expert), so each expert's packed weights stream from HBM once per
 // feature tile; 16-row sub-tiles past the expert's last row are skipped, so a
 // short tile costs MFMA issue in proportion to its real rows.
 //
-// Each workgroup (8 waves, two per SIMD) owns one token tile and one feature
-// tile.  The blockIdx -> work mapping is XCD aware: the dispatcher deals
-// workgroups round-robin to the 8 XCDs; each XCD gets an equal contiguous
-// share of the work items that exist, so neighbouring items (the feature tiles
-// of one token tile, which share its activation rows) sit on the same XCD and
-// its L2, and no XCD idles when the real tile count is below the grid bound.
+// Persistent workgroups: one per compute unit (its LDS ring allows no
+// second), 8 waves, two per SIMD.  The dispatcher deals workgroups
+// round-robin to the 8 XCDs; each XCD owns an equal contiguous share of the
+// items that exist, so the feature tiles of one token tile (which share its
+// activation rows) sit on one XCD and its L2, and a workgroup walks its XCD's
+// share with a fixed stride.  The LDS ring runs on across items: the last
+// three K-steps of an item already load the next item's first three stages
+// (and the row sources of the item after that), so the ring never drains and
+// the epilogue of one item overlaps the next item's first loads.
 //
 // K loop (one K-step = 128 elements): every operand of a K-step -- the
 // activation rows (kBM x 128 B, the 16-byte chunk index XOR-ed with the row's
@@ -164,18 +166,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup b is dispatched to XCD b % 8.  Give each XCD an equal contiguous
-// share of the W work items that exist (W is known on the device only; the
-// grid is sized for the host-known bound, nb >= W, nb a multiple of 8), so
-// that every XCD gets work and neighbouring items share one L2.  Returns -1
-// for a workgroup with nothing to do.
-__device__ __forceinline__ int xcd_work_item(int b, int W) {
-  const int per = (W + 7) >> 3;
-  const int r = b >> 3;
-  const int w = (b & 7) * per + r;
-  return (r < per && w < W) ? w : -1;
-}
-
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                           int E, int* __restrict__ hdr) {
   __shared__ int cnt[1024];
@@ -192,30 +182,53 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
   if (tid == 0) hdr[0] = total;
 }
 
-// One wave's share of the DMA loads of a stage.  Bases are wave-uniform and
-// at K-step 0 (each advances by a fixed stride per K-step), offsets per lane;
-// LDS offsets are relative to the stage and wave-uniform.
+// One wave's share of the DMA loads of a stage, the part that changes from
+// one work item to the next: bases at K-step 0 (each advances by a fixed
+// stride per K-step) and per-lane source offsets.  The LDS destinations and
+// strides follow from the wave index (issue_stage).
 struct Dma {
   const uint8_t* abase;  // activation rows
-  uint32_t aoff[3];      // this lane's chunk of row groups w, w+8, w+16
   const uint8_t* bbase;  // the wave's first weight tile
-  uint32_t boff[2];      // this lane's 16 bytes of its two tiles
-  const uint8_t* sbase;  // scales (skind != 0)
-  uint32_t soff;
-  uint32_t la[3], lb[2], ls;
-  int bstep;             // weight bytes per K-step
-  long sstep;            // scale bytes per K-step
-  int skind;             // 0: no scale load, 1: dword, 2: dwordx4 (wave-uniform)
+  const uint8_t* sbase;  // scales (waves 0-3)
+  uint32_t aoff[3];      // this lane's chunk of row groups w, w+8, w+16
+  uint32_t soff;         // this lane's scale bytes
 };
 
-__device__ __forceinline__ void issue_stage(const Dma& d, uint32_t stage_lds, int j) {
-  if (d.skind == 1)
-    dma_x1(d.sbase + (size_t)j * d.sstep, d.soff, stage_lds + d.ls);
-  else if (d.skind == 2)
-    dma_x4(d.sbase + (size_t)j * d.sstep, d.soff, stage_lds + d.ls);
-  dma_stage5(d.abase + (size_t)j * 128, d.aoff[0], d.aoff[1], d.aoff[2],
-             d.bbase + (size_t)j * d.bstep, d.boff[0], d.boff[1], stage_lds + d.la[0],
-             stage_lds + d.la[1], stage_lds + d.la[2], stage_lds + d.lb[0], stage_lds + d.lb[1]);
+// Wave-uniform values for the scalar operands of the DMA instructions (no-ops
+// when the compiler already holds them in scalar registers).
+__device__ __forceinline__ uint32_t wave_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const uint8_t* wave_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint64_t lo = wave_u32((uint32_t)v), hi = wave_u32((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uintptr_t)(lo | (hi << 32)));
+}
+
+// The per-wave constant part of the DMA: which scale load the wave issues
+// (0: none, 1: activation scale dwords, 2: weight scales as dwordx4), its
+// K-step stride and LDS offset within a stage, and the lane's weight offset.
+struct WaveDma {
+  int skind;
+  long sstep;
+  uint32_t ls;
+  uint32_t boff0;
+};
+
+// Stage j of descriptor d into the stage at LDS address stage_lds.  Wave w
+// writes activation row groups w, w+8, w+16 (1 KiB each at 1024 rg), weight
+// tiles 2w, 2w+1 (at kABytes + 1024 t), and its scale load (see WaveDma).
+template <bool kUp>
+__device__ __forceinline__ void issue_stage(const Dma& d, const WaveDma& c, uint32_t stage_lds_,
+                                            int j, int wave) {
+  const uint32_t stage_lds = wave_u32(stage_lds_);
+  if (c.skind == 1)
+    dma_x1(wave_ptr(d.sbase + (size_t)j * c.sstep), d.soff, stage_lds + c.ls);
+  else if (c.skind == 2)
+    dma_x4(wave_ptr(d.sbase + (size_t)j * c.sstep), d.soff, stage_lds + c.ls);
+  const uint32_t la = stage_lds + (uint32_t)(1024 * wave);
+  const uint32_t lb = stage_lds + (uint32_t)(kABytes + 2048 * wave);
+  dma_stage5(wave_ptr(d.abase + (size_t)j * 128), d.aoff[0], d.aoff[1], d.aoff[2],
+             wave_ptr(d.bbase + (size_t)j * (kUp ? 4096 : 2048)), c.boff0, c.boff0 + 1024u, la,
+             la + 8192u, la + 16384u, lb, lb + 1024u);
 }
 
 // Operand fragments of one K-step for a wave with N live sub-tiles: its 4
@@ -316,12 +329,130 @@ __device__ __forceinline__ void mfma_tail(const Head<N>& h, const Tail<N>& f, v4
     mfma_row<kUp, N>(f.a[i], f.sa[i], h, acc[FragsShape<N>::kHead + i]);
 }
 
+// Launch constants of a GEMM.  The kernel's prologue parks them in LDS and
+// each work item re-reads them there, so none holds a register across the
+// K-loop.  Weight block (e, g, j) (g: 32-row group, j: K-step) starts at
+// wbase + ((e*QG + g)*J + j) * 4096 (gate/up) or 2048 (down) bytes, its scales
+// at sbase + (...) * 256 or 128.
+struct KArgs {
+  const uint8_t* wbase;
+  const uint8_t* sbase;
+  const uint8_t* act;         // activations: x (gate/up) or h (down), fp8 rows of K bytes
+  const uint32_t* sT;         // activation scales by K-step
+  const int32_t* sorted_pair;
+  const int32_t* offsets;
+  const int* hdr;             // tile count, then the tile list at kTileHdr
+  uint8_t* hq;
+  uint8_t* hs;
+  uint16_t* O;
+  long P;
+  int k, NF, H, I, QG, J;
+};
+
+// One work item of a workgroup: a token tile (expert e, sorted rows m0 ..
+// m0 + rows) and a feature tile ft, with this wave's DMA descriptor for it.
+struct Item {
+  Dma d;
+  int e, m0, rows, ft;
+};
+
+// Tile of work item `it`: expert, first sorted row, rows, feature tile.  The
+// tile list and the offsets are not written by the GEMM kernels, so they are
+// read as constant memory: uniform scalar loads, whose wait is not the
+// vector-memory count (a vector load's wait would also wait for the ring's
+// DMA).
+__device__ __forceinline__ void item_tile(const int* __restrict__ hdr,
+                                          const int32_t* __restrict__ offsets, int NF, int it,
+                                          int& e, int& m0, int& rows, int& ft) {
+  typedef __attribute__((address_space(4))) const int32_t cint;  // read-only here
+  const int tile = __builtin_amdgcn_readfirstlane(it / NF);
+  ft = it - tile * NF;
+  cint* tl = (cint*)(reinterpret_cast<const uint8_t*>(hdr) + kTileHdr);
+  e = tl[2 * tile];
+  m0 = tl[2 * tile + 1];
+  rows = min(kBM, ((cint*)offsets)[e + 1] - m0);
+}
+
+// A pointer re-read from LDS, known again to address global memory, so that
+// accesses through it are global (not flat) instructions.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* as_global(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
+// The wave's DMA descriptor of an item.  rsrc (LDS, gate/up only) holds the
+// sorted pair index of each tile row, rows past the tile repeating the last
+// one; the token row is the pair index / k.  Down reads rows m0 .. of h in
+// sorted order, rows past the tile repeating the last.
+template <bool kUp>
+__device__ __forceinline__ void make_dma(Item& it, const int* rsrc, const KArgs& a, int wave,
+                                         int lane) {
+  Dma& d = it.d;
+  const int K = kUp ? a.H : a.I;
+  const int e = it.e, m0 = it.m0, rows = it.rows, ft = it.ft;
+  // Activations: row group rg = wave + 8u (u < 3) holds rows 8rg..8rg+7,
+  // 1 KiB at stage offset 1024 rg; lane l lands at row 8rg + l/8, physical
+  // chunk l%8, which holds logical chunk (l%8) ^ (l/8) (the row's low 3 bits
+  // are l/8).  Offsets are from the activation base (token rows for gate/up,
+  // the tile's first sorted row for down); rows past the tile load the last
+  // row again, and their products land in output rows that are never stored.
+  d.abase = kUp ? a.act : a.act + (size_t)m0 * K;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int r = 8 * (wave + 8 * u) + (lane >> 3);
+    const size_t src = kUp ? (size_t)(rsrc[r] / a.k) : (size_t)min(r, rows - 1);
+    d.aoff[u] = (uint32_t)(src * K) + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+  }
+  // Weights: stage tiles 2w, 2w+1 (1 KiB each, lane order = packed order),
+  // adjacent in the packed layout.  up: tile index 4g + t = q-group 4ft + g,
+  // tile t; down: tile index 2g2 + t = q2-group 8ft + g2, tile t (groups past
+  // H read group 0, whose products are never stored).
+  const size_t eJ = (size_t)e * a.QG;
+  if (kUp) {
+    d.bbase = a.wbase + (eJ + 4 * ft + (wave >> 1)) * a.J * 4096 + (size_t)(2 * (wave & 1)) * 1024;
+  } else {
+    const int g2 = 8 * ft + wave;
+    d.bbase = a.wbase + (eJ + (g2 < a.QG ? g2 : 0)) * a.J * 2048;
+  }
+  // Scales.  Waves 0-2: activation scale dwords of rows 64w..64w+63 (as[row])
+  // from the by-step array, one contiguous run per K-step (rows past the
+  // tile read its last row).  Wave 3: all weight scales of the K-step as one
+  // dwordx4 load, 16 bytes per lane: up: lanes 16g..16g+15 take q-group
+  // 4ft + g's 256 bytes (bs[64g + d]); down: lanes 8g2..8g2+7 take q2-group
+  // 8ft + g2's 128 bytes (bs[32 g2 + d]).
+  if (wave < 3) {
+    d.sbase = reinterpret_cast<const uint8_t*>(a.sT + m0);
+    d.soff = (uint32_t)(min(64 * wave + lane, rows - 1) * 4);
+  } else if (wave == 3) {
+    if (kUp) {
+      d.sbase = a.sbase + (eJ + 4 * ft) * a.J * 256;
+      d.soff = (uint32_t)((lane >> 4) * a.J * 256 + (lane & 15) * 16);
+    } else {
+      const int g2 = 8 * ft + (lane >> 3);
+      d.sbase = a.sbase + (eJ + 8 * ft) * a.J * 128;
+      d.soff = (uint32_t)((g2 < a.QG ? (lane >> 3) : 0) * a.J * 128 + (lane & 7) * 16);
+    }
+  } else {
+    d.sbase = a.wbase;
+    d.soff = 0;
+  }
+  // the bases are uniform: keep them in scalar registers
+  d.abase = wave_ptr(d.abase);
+  d.bbase = wave_ptr(d.bbase);
+  d.sbase = wave_ptr(d.sbase);
+}
+
+// One work item with N live sub-tiles on this wave.  The K-loop keeps three
+// stages of the ring in flight (stage s of the item in ring slot
+// (base + s) % kRing).  Stages s >= J are the next item's stages s - J when
+// chain is set (the next item then starts primed: its stages 0-2 issued and
+// stage 0 published by this item's last barrier), else the last stage again,
+// never read.
 template <bool kUp, int N>
-__device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st, int J, int lane,
-                                          int wm, int wn, int rows, int m0, int ft, int I, int H,
-                                          int QG2,
-                                          uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
-                                          uint16_t* __restrict__ O) {
+__device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int base, bool primed,
+                                         bool chain, const Lds& o, const WaveDma& wd, Stage* st,
+                                         int J, int lane, int wave, const KArgs& ka) {
+  const int wm = wave >> 2, wn = wave & 3;
   v4f acc[N > 0 ? N : 1][4];
 #pragma unroll
   for (int i = 0; i < N; ++i)
@@ -329,20 +460,28 @@ __device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st,
     for (int t = 0; t < 4; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t ring = (uint32_t)(uintptr_t)(lds_u8*)st;
-  // stage s goes to slot s % kRing; stages past the last load the last again
   auto issue = [&](int s) {
-    issue_stage(d, ring + (uint32_t)(s % kRing) * (uint32_t)sizeof(Stage), min(s, J - 1));
+    const bool nx = s >= J && chain;
+    Dma d;
+    d.abase = nx ? nxt.d.abase : cur.d.abase;
+    d.bbase = nx ? nxt.d.bbase : cur.d.bbase;
+    d.sbase = nx ? nxt.d.sbase : cur.d.sbase;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) d.aoff[u] = nx ? nxt.d.aoff[u] : cur.d.aoff[u];
+    d.soff = nx ? nxt.d.soff : cur.d.soff;
+    issue_stage<kUp>(d, wd, ring + (uint32_t)((base + s) % kRing) * (uint32_t)sizeof(Stage),
+                     s < J ? s : (nx ? s - J : J - 1), wave);
   };
   // Step j multiplies stage j from registers (head hc read during step j-1,
   // tail read here).  Stages issued before its barrier run up to j + 2, so
   // stage j+1 is complete once at most one stage of this wave's loads is
-  // outstanding; the barrier then publishes it to every wave and retires slot
-  // j % kRing (every wave's reads of stage j precede it), which takes stage
-  // j + 3.
+  // outstanding (loads issued after it only lengthen the wait); the barrier
+  // then publishes it to every wave and retires the slot of stage j (every
+  // wave's reads of stage j precede it), which takes stage j + 3.
   auto step = [&](int j, Head<N>& hc, Head<N>& hn) {
     Tail<N> tl;
-    const uint8_t* Sc = reinterpret_cast<const uint8_t*>(&st[j % kRing]);
-    const uint8_t* Sn = reinterpret_cast<const uint8_t*>(&st[(j + 1) % kRing]);
+    const uint8_t* Sc = reinterpret_cast<const uint8_t*>(&st[(base + j) % kRing]);
+    const uint8_t* Sn = reinterpret_cast<const uint8_t*>(&st[(base + j + 1) % kRing]);
     if constexpr (N > 0) read_tail<N>(tl, Sc, o);
     if constexpr (N > 0) mfma_head<kUp, N>(hc, acc);
     wait_vmcnt<kOps>();
@@ -351,13 +490,15 @@ __device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st,
     issue(j + kRing);
     if constexpr (N > 0) mfma_tail<kUp, N>(hc, tl, acc);
   };
-  issue(0);
-  issue(1);
-  issue(2);
+  if (!primed) {  // cold start: fill the ring and wait for stage 0
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vmcnt<2 * kOps>();
+    __syncthreads();
+  }
   Head<N> h0, h1;
-  wait_vmcnt<2 * kOps>();
-  __syncthreads();
-  if constexpr (N > 0) read_head<kUp, N>(h0, reinterpret_cast<const uint8_t*>(&st[0]), o);
+  if constexpr (N > 0) read_head<kUp, N>(h0, reinterpret_cast<const uint8_t*>(&st[base % kRing]), o);
   int j = 0;
   if (J & 1) {  // odd J: one step first, so the loop below takes steps in pairs
     step(0, h0, h1);
@@ -368,15 +509,17 @@ __device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st,
     step(j, h0, h1);
     step(j + 1, h1, h0);
   }
-  // no LDS-DMA may still be writing when the workgroup's LDS is released
-  wait_vmcnt<0>();
 
+  const int H = ka.H, I = ka.I, QG2 = ka.H / 32;
+  auto* __restrict__ hq = as_global(ka.hq);
+  auto* __restrict__ hs = as_global(ka.hs);
+  auto* __restrict__ O = as_global(ka.O);
   // lane holds rows 4*(lane>>4)+v of each 16-row sub-tile, column lane&15 of each tile
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int rbase = 16 * (wm + 2 * i) + 4 * (lane >> 4);
     if (kUp) {
-      const int q = 4 * ft + wn;  // 32-feature group of I
+      const int q = 4 * cur.ft + wn;  // 32-feature group of I
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float h0 = silu_mul(acc[i][0][v], acc[i][2][v]);
@@ -385,28 +528,30 @@ __device__ __forceinline__ void gemm_body(const Dma& d, const Lds& o, Stage* st,
         float mul;
         const uint32_t sc = mx_scale_from_amax(am, &mul);
         const int r = rbase + v;
-        if (r < rows) {
-          uint8_t* hrow = hq + (size_t)(m0 + r) * I + q * 32 + (lane & 15);
+        if (r < cur.rows) {
+          auto* hrow = hq + (size_t)(cur.m0 + r) * I + q * 32 + (lane & 15);
           hrow[0] = (uint8_t)f32_to_e4m3(h0 * mul);
           hrow[16] = (uint8_t)f32_to_e4m3(h1 * mul);
-          if ((lane & 15) == 0) hs[(size_t)(m0 + r) * (I / 32) + q] = (uint8_t)sc;
+          if ((lane & 15) == 0) hs[(size_t)(cur.m0 + r) * (I / 32) + q] = (uint8_t)sc;
         }
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int g2 = 8 * ft + 2 * wn + (t >> 1);
+        const int g2 = 8 * cur.ft + 2 * wn + (t >> 1);
         if (g2 >= QG2) continue;
         const int col = g2 * 32 + (t & 1) * 16 + (lane & 15);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = rbase + v;
-          if (r < rows) O[(size_t)(m0 + r) * H + col] = f32_to_bf16(acc[i][t][v]);
+          if (r < cur.rows) O[(size_t)(cur.m0 + r) * H + col] = f32_to_bf16(acc[i][t][v]);
         }
       }
     }
   }
 }
+
+
 
 // Activation scales by K-step: sT[j][p] = the dword of E8M0 codes of K-step j
 // (4 blocks of 32) of sorted row p, taken from row sorted_pair[p] / k of the
@@ -425,97 +570,49 @@ __global__ __launch_bounds__(256) void scales_by_step_kernel(const uint32_t* __r
 
 // kUp: gate/up GEMM (A = x rows gathered by token, K = H; B = W1/W3; epilogue
 // SwiGLU + MXFP8 of h).  !kUp: down GEMM (A = h rows in sorted order, K = I;
-// B = W2; epilogue bf16 store of O).
+// B = W2; epilogue bf16 store of O).  Persistent: one workgroup per CU walks
+// its share of the work items.  Workgroup b is dispatched to XCD b % 8; XCD x
+// owns items [x*per, (x+1)*per) (per = ceil(W/8), W known on the device
+// only), so the feature tiles of one token tile, which share its activation
+// rows, stay on one XCD and its L2; its r-th workgroup takes items
+// x*per + r, + G/8, ... (G = the grid).
 template <bool kUp>
-__global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
-    const uint8_t* __restrict__ packed, PackedLayout L, const uint8_t* __restrict__ act,
-    const uint32_t* __restrict__ sT, long P, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pair, int k, const int* __restrict__ hdr, int NF,
-    int nblocks, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ O) {
+__global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(KArgs args) {
   __shared__ __align__(16) Stage st[kRing];
-  __shared__ int row_src[kBM];
-  const int logical = xcd_work_item(blockIdx.x, hdr[0] * NF);
-  if (logical < 0) return;
-  const int tile = logical / NF, ft = logical % NF;
-  const int2 td = reinterpret_cast<const int2*>(reinterpret_cast<const uint8_t*>(hdr) + kTileHdr)[tile];
-  const int e = td.x, m0 = td.y;
-  const int rows = min(kBM, offsets[e + 1] - m0);
-  const int tid = threadIdx.x;
-  const int H = L.H, I = L.I;
-  const int K = kUp ? H : I;  // reduction length
-  const int QG2 = H / 32;     // 32-row groups of the down weights
-  // source row of each tile row; rows past the tile read row 0's data, whose
-  // products land in output rows that are never stored
-  if (tid < kBM) row_src[tid] = (tid < rows) ? (kUp ? sorted_pair[m0 + tid] / k : m0 + tid) : -1;
-  __syncthreads();
-  const int row0 = row_src[0];
+  __shared__ int rsrc[3][kBM];
+  __shared__ KArgs ka;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) ka = args;
+  const int W = args.hdr[0] * args.NF;
+  const int per = (W + 7) >> 3;
+  const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3;
+  const int end = min((xcd + 1) * per, W);
+  int it = xcd * per + (int)(blockIdx.x >> 3);
+  if (it >= end) return;
 
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int wm = wave >> 2, wn = wave & 3;
+  const int J = args.J;
+  const long P = args.P;
 
-  Dma d;
-  // Activations: row group rg = wave + 8u (u < 3) holds rows 8rg..8rg+7,
-  // 1 KiB at stage offset 1024 rg; lane l lands at row 8rg + l/8, physical
-  // chunk l%8, which holds logical chunk (l%8) ^ (l/8) (the row's low 3 bits
-  // are l/8).  Offsets are from the activation base (token rows for gate/up,
-  // the tile's first sorted row for down).
-  d.abase = kUp ? act : act + (size_t)m0 * K;
-#pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int rg = wave + 8 * u;
-    const int r = 8 * rg + (lane >> 3);
-    const int src = row_src[r] >= 0 ? row_src[r] : row0;
-    d.aoff[u] = (uint32_t)((kUp ? (size_t)src : (size_t)(src - m0)) * K) + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
-    d.la[u] = (uint32_t)(1024 * rg);
-  }
-  // Weights: stage tiles 2w, 2w+1 (1 KiB each, lane order = packed order),
-  // adjacent in the packed layout.  up: tile index 4g + t = q-group 4ft + g,
-  // tile t; down: tile index 2g2 + t = q2-group 8ft + g2, tile t (groups past
-  // H read group 0, whose products are never stored).
+  // Row sources (gate/up): rsrc[q % 3] holds those of the workgroup's q-th
+  // item.  The first two come by plain loads; with chaining, item q + 2's
+  // come by one LDS-DMA dword per lane from waves 0-2 at the start of item q,
+  // before its stage 3, so item q's step-1 wait and barrier cover them before
+  // item q + 1 builds its successor's descriptor from them.
+  Item cur, nxt;
+  item_tile(args.hdr, args.offsets, args.NF, it, cur.e, cur.m0, cur.rows, cur.ft);
   if (kUp) {
-    d.bbase = packed + L.upw_block(e, 4 * ft + (wave >> 1), 0) + (size_t)(2 * (wave & 1)) * 1024;
-  } else {
-    const int g2 = 8 * ft + wave;
-    d.bbase = packed + L.dnw_block(e, g2 < QG2 ? g2 : 0, 0);
-  }
-  d.boff[0] = (uint32_t)(lane * 16);
-  d.boff[1] = (uint32_t)(lane * 16 + 1024);
-  d.lb[0] = (uint32_t)(kABytes + 2048 * wave);
-  d.lb[1] = (uint32_t)(kABytes + 2048 * wave + 1024);
-  d.bstep = kUp ? 4096 : 2048;
-  // Scales.  Waves 0-2: activation scale dwords of rows 64w..64w+63 (as[row])
-  // from the by-step array, one contiguous run per K-step (rows past the
-  // tile read its last row).  Wave 3: all weight scales of the K-step as one
-  // dwordx4 load, 16 bytes per lane: up: lanes 16g..16g+15 take q-group
-  // 4ft + g's 256 bytes (bs[64g + d]); down: lanes 8g2..8g2+7 take q2-group
-  // 8ft + g2's 128 bytes (bs[32 g2 + d]).
-  if (wave < 3) {
-    d.sbase = reinterpret_cast<const uint8_t*>(sT + m0);
-    d.soff = (uint32_t)(min(64 * wave + lane, rows - 1) * 4);
-    d.sstep = P * 4;
-    d.ls = (uint32_t)(kABytes + kBBytes + 256 * wave);
-    d.skind = 1;
-  } else if (wave == 3) {
-    if (kUp) {
-      d.sbase = packed + L.ups_block(e, 4 * ft, 0);
-      d.soff = (uint32_t)((lane >> 4) * L.J * 256 + (lane & 15) * 16);
-      d.sstep = 256;
-    } else {
-      const int g2 = 8 * ft + (lane >> 3);
-      d.sbase = packed + L.dns_block(e, 8 * ft, 0);
-      d.soff = (uint32_t)((g2 < QG2 ? (lane >> 3) : 0) * L.J2 * 128 + (lane & 7) * 16);
-      d.sstep = 128;
+    if (tid < kBM) rsrc[0][tid] = args.sorted_pair[cur.m0 + min(tid, cur.rows - 1)];
+    if (it + stride < end) {
+      int e1, m1, r1, f1;
+      item_tile(args.hdr, args.offsets, args.NF, it + stride, e1, m1, r1, f1);
+      if (tid < kBM) rsrc[1][tid] = args.sorted_pair[m1 + min(tid, r1 - 1)];
     }
-    d.ls = (uint32_t)(kABytes + kBBytes + kBM * 4);
-    d.skind = 2;
-  } else {
-    d.sbase = nullptr;
-    d.soff = 0;
-    d.sstep = 0;
-    d.ls = 0;
-    d.skind = 0;
   }
+  __syncthreads();
+  make_dma<kUp>(cur, rsrc[0], args, wave, lane);
+
   // LDS read offsets of this lane's fragments (see Lds)
   Lds o;
   {
@@ -533,22 +630,58 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(
     }
   }
 
-  const int J = K / 128;
-  const int nsub = (rows + 15) / 16;  // live 16-row sub-tiles of the tile
-  int nact = 0;                       // this wave's live sub-tiles: i = 0..nact-1
+  WaveDma wd;
+  wd.skind = wave < 3 ? 1 : (wave == 3 ? 2 : 0);
+  wd.sstep = wave < 3 ? P * 4 : (kUp ? 256 : 128);
+  wd.ls = (uint32_t)(wave < 3 ? kABytes + kBBytes + 256 * wave : kABytes + kBBytes + kBM * 4);
+  wd.boff0 = (uint32_t)(lane * 16);
+
+  int base = 0;
+  bool primed = false;
+  for (int q = 0;; ++q) {
+    const int nit = it + stride;
+    const bool has_next = nit < end;
+    const bool chain = has_next && J >= 4;
+    if (has_next) {
+      item_tile(args.hdr, args.offsets, args.NF, nit, nxt.e, nxt.m0, nxt.rows, nxt.ft);
+      if (kUp && !chain && q > 0) {  // short K, no chaining: plain loads
+        if (tid < kBM) rsrc[(q + 1) % 3][tid] = as_global(ka.sorted_pair)[nxt.m0 + min(tid, nxt.rows - 1)];
+        __syncthreads();
+      }
+      make_dma<kUp>(nxt, rsrc[(q + 1) % 3], ka, wave, lane);
+    }
+    if (kUp && chain && nit + stride < end && wave < 3) {
+      int e2, m2, r2, f2;
+      item_tile(args.hdr, args.offsets, args.NF, nit + stride, e2, m2, r2, f2);
+      dma_x1(wave_ptr(reinterpret_cast<const uint8_t*>(ka.sorted_pair + m2)),
+             (uint32_t)(min(64 * wave + lane, r2 - 1) * 4),
+             wave_u32((uint32_t)(uintptr_t)(lds_u8*)rsrc[(q + 2) % 3] + 256u * (uint32_t)wave));
+    }
+    const int nsub = (cur.rows + 15) / 16;  // live 16-row sub-tiles of the tile
+    int nact = 0;                           // this wave's live sub-tiles: i = 0..nact-1
 #pragma unroll
-  for (int i = 0; i < kBM / 32; ++i)
-    if (wm + 2 * i < nsub) nact = i + 1;
-  nact = __builtin_amdgcn_readfirstlane(nact);
-  switch (nact) {
-    case 0: gemm_body<kUp, 0>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 1: gemm_body<kUp, 1>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 2: gemm_body<kUp, 2>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 3: gemm_body<kUp, 3>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 4: gemm_body<kUp, 4>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    case 5: gemm_body<kUp, 5>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
-    default: gemm_body<kUp, 6>(d, o, st, J, lane, wm, wn, rows, m0, ft, I, H, QG2, hq, hs, O); break;
+    for (int i = 0; i < kBM / 32; ++i)
+      if (wm + 2 * i < nsub) nact = i + 1;
+    nact = __builtin_amdgcn_readfirstlane(nact);
+#define MOE_RUN(NN) run_item<kUp, NN>(cur, nxt, base, primed, chain, o, wd, st, J, lane, wave, ka)
+    switch (nact) {
+      case 0: MOE_RUN(0); break;
+      case 1: MOE_RUN(1); break;
+      case 2: MOE_RUN(2); break;
+      case 3: MOE_RUN(3); break;
+      case 4: MOE_RUN(4); break;
+      case 5: MOE_RUN(5); break;
+      default: MOE_RUN(6); break;
+    }
+#undef MOE_RUN
+    if (!has_next) break;
+    base = (base + J) % kRing;
+    primed = chain;
+    cur = nxt;
+    it = nit;
   }
+  // no LDS-DMA may still be writing when the workgroup's LDS is released
+  wait_vmcnt<0>();
 }
 
 long max_tiles(long P, int E) { return (P + kBM - 1) / kBM + E; }
@@ -557,6 +690,21 @@ size_t align256_(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // workspace: tile header and list, then the by-step activation scales
 size_t tile_list_bytes(long P, int E) { return align256_(kTileHdr + (size_t)max_tiles(P, E) * 8); }
+
+// One workgroup per compute unit (the kernel's LDS allows no more), rounded
+// down to whole rounds of the 8 XCDs; queried once per device.
+unsigned persistent_grid() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
+      ncu = 256;
+    cached[dev] = ncu / 8 * 8;
+  }
+  return (unsigned)cached[dev];
+}
 
 }  // namespace
 
@@ -576,9 +724,25 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
   hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 255) / 256), (unsigned)L.J), dim3(256),
                      0, s, reinterpret_cast<const uint32_t*>(xs), L.J, sorted_pair, k, P, sT);
   const int NF = L.I / 128;
-  const long nb = (max_tiles(P, L.E) * NF + 7) / 8 * 8;
-  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)nb), dim3(kThreads), 0, s, packed, L,
-                     xq, sT, P, offsets, sorted_pair, k, hdr, NF, (int)nb, hq, hs, (uint16_t*)nullptr);
+  KArgs a;
+  a.wbase = packed + L.upw_off;
+  a.sbase = packed + L.ups_off;
+  a.act = xq;
+  a.sT = sT;
+  a.sorted_pair = sorted_pair;
+  a.offsets = offsets;
+  a.hdr = hdr;
+  a.hq = hq;
+  a.hs = hs;
+  a.O = nullptr;
+  a.P = P;
+  a.k = k;
+  a.NF = NF;
+  a.H = L.H;
+  a.I = L.I;
+  a.QG = L.I / 32;
+  a.J = L.J;
+  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(persistent_grid()), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -592,10 +756,25 @@ hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, con
   hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 255) / 256), (unsigned)L.J2), dim3(256),
                      0, s, reinterpret_cast<const uint32_t*>(hs), L.J2, (const int32_t*)nullptr, k, P, sT);
   const int NF = (L.H + 255) / 256;
-  const long nb = (max_tiles(P, L.E) * NF + 7) / 8 * 8;
-  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)nb), dim3(kThreads), 0, s, packed,
-                     L, hq, sT, P, offsets, (const int32_t*)nullptr, k, hdr, NF, (int)nb,
-                     (uint8_t*)nullptr, (uint8_t*)nullptr, O);
+  KArgs a;
+  a.wbase = packed + L.dnw_off;
+  a.sbase = packed + L.dns_off;
+  a.act = hq;
+  a.sT = sT;
+  a.sorted_pair = nullptr;
+  a.offsets = offsets;
+  a.hdr = hdr;
+  a.hq = nullptr;
+  a.hs = nullptr;
+  a.O = O;
+  a.P = P;
+  a.k = k;
+  a.NF = NF;
+  a.H = L.H;
+  a.I = L.I;
+  a.QG = L.H / 32;
+  a.J = L.J2;
+  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(persistent_grid()), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
