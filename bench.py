@@ -209,6 +209,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="1 = force decode path, 2 = force prefill path")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 = skip")
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0 = auto)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the layer call (one graph per weight copy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 20 plain 1 GiB device copies (HBM counter calibration)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="PATH",
@@ -287,6 +289,21 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.graph:
+        # the layer call only enqueues kernels on the current stream (no allocation,
+        # memset or host readback), so one call per weight copy is captured and replayed
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                moe.layer_forward(pws[c], x, logits, k, args.flags, y=y, workspace=lws)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+
+        def step(i):  # noqa: F811
+            graphs[i % copies].replay()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i)
@@ -339,7 +356,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": synth.CONFIG_NAMES.get(args.config, args.config), "T": T, "H": H, "I": I,
                    "E": E, "k": k, "seed": sh.seed, "used_experts": used, "weight_copies": copies,
-                   "path_flags": args.flags},
+                   "path_flags": args.flags, "launch": "hip_graph" if args.graph else "eager"},
         "layer_hbm_tbps": b_layer / (ms_per_step * 1e-3) / 1e12,
         "layer_hbm_frac": b_layer / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_mfma_frac_fp8": flops / (ms_per_step * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
