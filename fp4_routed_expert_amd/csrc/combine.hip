@@ -3,7 +3,8 @@
 // reduction order, pwwt.cn review section 4.2).  O holds the expert outputs
 // as bf16 (a matrix-multiply output kept at low precision, its sum in fp32:
 // the same review, section 4.1).  Each thread produces four consecutive
-// outputs from 64-bit loads of O and one 128-bit store; bandwidth bound.
+// outputs from 64-bit loads of O and one 128-bit store; bandwidth bound at
+// prefill sizes, latency bound at decode sizes (hence the batched loads).
 #include "common.h"
 
 namespace moe {
@@ -20,13 +21,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint2* __restrict__ 
   const int c = blockIdx.y * blockDim.x + threadIdx.x;
   if (c >= H4) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float g = gates[(size_t)t * k + j];
-    const uint2 o = O[(size_t)pair_pos[(size_t)t * k + j] * H4 + c];
-    acc.x = fmaf(g, bf16_lo(o.x), acc.x);
-    acc.y = fmaf(g, bf16_hi(o.x), acc.y);
-    acc.z = fmaf(g, bf16_lo(o.y), acc.z);
-    acc.w = fmaf(g, bf16_hi(o.y), acc.w);
+  // slots in batches of 8: all their row indices and gates, then all their O
+  // loads, are in flight together (a short last batch repeats its last slot's
+  // loads and skips their sums); the sum still runs in slot order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    const int n = min(8, k - j0);
+    int row[8];
+    float g[8];
+    uint2 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t idx = (size_t)t * k + j0 + min(u, n - 1);
+      row[u] = pair_pos[idx];
+      g[u] = gates[idx];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = O[(size_t)row[u] * H4 + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 a = make_float4(fmaf(g[u], bf16_lo(o[u].x), acc.x), fmaf(g[u], bf16_hi(o[u].x), acc.y),
+                                   fmaf(g[u], bf16_lo(o[u].y), acc.z), fmaf(g[u], bf16_hi(o[u].y), acc.w));
+      if (u < n) acc = a;
+    }
   }
   y[(size_t)t * H4 + c] = acc;
 }
