@@ -58,6 +58,9 @@ def _load():
         lib.orc_route.argtypes = [p, i64, i32, i32, p, p]
         lib.orc_sort.argtypes = [p, i64, i32, p, p, p, p]
         lib.orc_expert_gate_up.argtypes = [p, p, i32, i32, p, p, p, p, p, p]
+        lib.orc_router_logits.argtypes = [p, p, i64, i32, i32, p, p]
+        lib.orc_layer_tokens_shared.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p, p, p, i32,
+                                                p, p, p, p, p, p, p, i64, p]
         lib.orc_swiglu_requant.argtypes = [p, p, i32, p, p, p]
         lib.orc_expert_down.argtypes = [p, p, i32, i32, p, p, p]
         lib.orc_layer_tokens.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p, p, p,
@@ -224,4 +227,40 @@ def layer_tokens(inp, tokens=None, want_pairs: bool = False):
                              _p(toks), n, _p(y), _p(h), _p(hq), _p(hs))
     if want_pairs:
         return y, h, hq, hs
+    return y
+
+
+# ------------------------------------------------- router and shared expert
+def router_logits(x_bits: np.ndarray, wg_bits: np.ndarray):
+    """Exact router logits x . Wg[e] (fp64) of bf16 operands and the absolute
+    sums that bound any fp32 evaluation's rounding error: ([T, E], [T, E])."""
+    x = _c(x_bits, np.uint16)
+    wg = _c(wg_bits, np.uint16)
+    T, H = x.shape
+    E = wg.shape[0]
+    assert wg.shape[1] == H
+    logit = np.empty((T, E), dtype=np.float64)
+    absum = np.empty((T, E), dtype=np.float64)
+    _load().orc_router_logits(_p(x), _p(wg), T, H, E, _p(logit), _p(absum))
+    return logit, absum
+
+
+def layer_tokens_shared(inp, logits, shared, tokens=None):
+    """y rows of the layer with routing on the given fp32 logits [T, E] and, if
+    ``shared`` = (w1, s1, w3, s3, w2, s2) of one expert is not None, that
+    expert's output added after the k routed slots."""
+    sh = inp.shape
+    T, H, I, E, k = sh.T, sh.H, sh.I, sh.E, sh.k
+    toks = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
+    y = np.empty((toks.size, H), dtype=np.float32)
+    if shared is None:
+        sp = [None] * 6
+        Is = 0
+    else:
+        sp = [_c(a, np.uint8) for a in shared]
+        Is = sp[0].shape[-2]
+    _load().orc_layer_tokens_shared(
+        _p(_c(inp.x, np.uint16)), _p(_c(logits, np.float32)), H, I, E, k,
+        _p(inp.w1), _p(inp.s1), _p(inp.w3), _p(inp.s3), _p(inp.w2), _p(inp.s2), Is,
+        *[(None if a is None else _p(a)) for a in sp], _p(toks), toks.size, _p(y))
     return y

@@ -301,3 +301,76 @@ void orc_layer_tokens(const uint16_t* x, const float* logits, int H, int I, int 
   free(ids); free(gates); free(xq); free(xs); free(G); free(U);
   free(h); free(hq); free(hs); free(O); free(acc);
 }
+
+/* --------------------------------------------- router and shared expert */
+
+/* Router logits ahead of the top-k (the gate network's first layer, which the
+ * pwwt.cn review, section 4.1, lets run at low precision while the top-k
+ * compare stays fp32): logit[t,e] = sum_h x[t,h] * Wg[e,h] with x and Wg in
+ * bf16.  Each product of two bf16 values is exact in fp64 and the sum is
+ * taken in fp64 in index order.  absum[t,e] = sum_h |x[t,h] * Wg[e,h]| bounds
+ * the rounding error of any fp32 evaluation of the same sum. */
+void orc_router_logits(const uint16_t* x, const uint16_t* wg, long T, int H, int E,
+                       double* logit, double* absum) {
+#pragma omp parallel for schedule(static)
+  for (long t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0, a = 0.0;
+      for (int h = 0; h < H; ++h) {
+        const double p = orc_bf16(x[t * (long)H + h]) * orc_bf16(wg[(long)e * H + h]);
+        s += p;
+        a += fabs(p);
+      }
+      logit[t * E + e] = s;
+      absum[t * E + e] = a;
+    }
+  }
+}
+
+/* The layer with a shared expert: the routed part exactly as orc_layer_tokens,
+ * then one more expert FFN (weights w1s..s2s, intermediate size Is) on the same
+ * MXFP8 row x_t, added with weight 1 after the k routed slots:
+ * y_t = sum_{j=0..k-1, in order} g_j * O_j + O_shared.  y is [ntok, H]. */
+void orc_layer_tokens_shared(const uint16_t* x, const float* logits, int H, int I, int E, int k,
+                             const uint8_t* w1, const uint8_t* s1, const uint8_t* w3,
+                             const uint8_t* s3, const uint8_t* w2, const uint8_t* s2, int Is,
+                             const uint8_t* w1s, const uint8_t* s1s, const uint8_t* w3s,
+                             const uint8_t* s3s, const uint8_t* w2s, const uint8_t* s2s,
+                             const int32_t* tokens, long ntok, float* y) {
+  const size_t wup = (size_t)I * (H / 2), sup = (size_t)I * (H / 32);
+  const size_t wdn = (size_t)H * (I / 2), sdn = (size_t)H * (I / 32);
+  const int Imax = I > Is ? I : Is;
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  float* gates = (float*)malloc(sizeof(float) * (size_t)k);
+  uint8_t* xq = (uint8_t*)malloc((size_t)H);
+  uint8_t* xs = (uint8_t*)malloc((size_t)H / 32);
+  double* G = (double*)malloc(sizeof(double) * (size_t)Imax);
+  double* U = (double*)malloc(sizeof(double) * (size_t)Imax);
+  float* h = (float*)malloc(sizeof(float) * (size_t)Imax);
+  uint8_t* hq = (uint8_t*)malloc((size_t)Imax);
+  uint8_t* hs = (uint8_t*)malloc((size_t)Imax / 32);
+  double* O = (double*)malloc(sizeof(double) * (size_t)H);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+  for (long n = 0; n < ntok; ++n) {
+    long t = tokens[n];
+    orc_route_token(logits + t * E, E, k, ids, gates);
+    orc_quant_mxfp8_bf16(x + t * (long)H, 1, H, xq, xs);
+    for (int r = 0; r < H; ++r) acc[r] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      size_t e = (size_t)ids[j];
+      orc_expert_gate_up(xq, xs, H, I, w1 + e * wup, s1 + e * sup, w3 + e * wup, s3 + e * sup, G, U);
+      orc_swiglu_requant(G, U, I, h, hq, hs);
+      orc_expert_down(hq, hs, H, I, w2 + e * wdn, s2 + e * sdn, O);
+      for (int r = 0; r < H; ++r) acc[r] += (double)gates[j] * O[r];
+    }
+    if (w1s) {
+      orc_expert_gate_up(xq, xs, H, Is, w1s, s1s, w3s, s3s, G, U);
+      orc_swiglu_requant(G, U, Is, h, hq, hs);
+      orc_expert_down(hq, hs, H, Is, w2s, s2s, O);
+      for (int r = 0; r < H; ++r) acc[r] += O[r];
+    }
+    for (int r = 0; r < H; ++r) y[n * (long)H + r] = (float)acc[r];
+  }
+  free(ids); free(gates); free(xq); free(xs); free(G); free(U);
+  free(h); free(hq); free(hs); free(O); free(acc);
+}

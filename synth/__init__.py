@@ -29,6 +29,9 @@ _SO = os.path.join(_HERE, "libsynth.so")
 
 # tensor ids of the counter-based generator
 TID_X, TID_LOGITS, TID_ZIPF, TID_W1, TID_S1, TID_W3, TID_S3, TID_W2, TID_S2 = range(9)
+# the router weights and the shared expert's weights (one more expert in the
+# same format as the routed ones)
+TID_WG, TID_SW1, TID_SS1, TID_SW3, TID_SS3, TID_SW2, TID_SS2 = range(9, 16)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -199,3 +202,22 @@ def make_inputs(cfg, probe_w2: bool = False, with_weights: bool = True, **overri
     if with_weights:
         li.w1, li.s1, li.w3, li.s3, li.w2, li.s2 = make_weights(sh, probe_w2)
     return li
+
+
+def make_router_weights(sh: Shape) -> np.ndarray:
+    """Router weights Wg as bf16 bits [E, H]: N(0, 1/H), so that with N(0, sigma)
+    activations the logits x . Wg[e] are about N(0, sigma^2)."""
+    return f32_to_bf16_bits(normal_f32(sh.seed, TID_WG, (sh.E, sh.H), 1.0 / np.sqrt(sh.H)))
+
+
+def make_shared_weights(sh: Shape, I_shared: int | None = None):
+    """One shared expert (E = 1) in the routed experts' format, intermediate size
+    I_shared (default I): w1, s1, w3, s3 [1, Is, H/2 | H/32], w2, s2 [1, H, Is/2 | Is/32]."""
+    H, Is = sh.H, (sh.I if I_shared is None else I_shared)
+    w1 = random_bytes(sh.seed, TID_SW1, (1, Is, H // 2))
+    s1 = uniform_codes(sh.seed, TID_SS1, (1, Is, H // 32), 121, 125)
+    w3 = random_bytes(sh.seed, TID_SW3, (1, Is, H // 2))
+    s3 = uniform_codes(sh.seed, TID_SS3, (1, Is, H // 32), 121, 125)
+    w2 = random_bytes(sh.seed, TID_SW2, (1, H, Is // 2))
+    s2 = uniform_codes(sh.seed, TID_SS2, (1, H, Is // 32), 121, 125)
+    return w1, s1, w3, s3, w2, s2
