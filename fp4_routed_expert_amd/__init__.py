@@ -22,7 +22,9 @@ from ._lib import (MOE_FLAG_FORCE_DECODE, MOE_FLAG_FORCE_PREFILL, MoeError,  # n
 __all__ = [
     "route_topk", "sort_permute", "quant_act_mxfp8", "prepack_weights", "PackedWeights",
     "expert_up", "expert_down", "combine", "grouped_forward", "moe_layer",
-    "forward_workspace_size", "layer_forward", "layer_workspace_size", "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
+    "forward_workspace_size", "layer_forward", "layer_workspace_size", "router_logits",
+    "shared_workspace_size", "shared_expert", "combine_shared", "layer_full_workspace_size",
+    "layer_forward_full", "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
 ]
 
 
@@ -242,4 +244,79 @@ def moe_layer(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: int, 
     if return_intermediates:
         return y, dict(topk_ids=ids, topk_gates=gates, expert_counts=counts, expert_offsets=offsets,
                        sorted_pair=sp, pair_pos=pp, xq=xq, xs=xs)
+    return y
+
+
+# ----------------------------------------------------- router and shared expert
+def router_logits(x: torch.Tensor, router_w: torch.Tensor, logits=None):
+    """logits [T, E] fp32 = x [T, H] bf16 . router_w [E, H] bf16^T (fp32 accumulation)."""
+    _check_dtype(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
+    _check_dtype(router_w, (torch.bfloat16, torch.int16, torch.uint16), "router_w")
+    T, H = x.shape
+    E, H2 = router_w.shape
+    if H2 != H:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, router_w {tuple(router_w.shape)}")
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check_dtype(logits, (torch.float32,), "logits")
+    _lib.check(_lib.lib().moe_router_logits(_ptr(x), _ptr(router_w), T, H, E, _ptr(logits),
+                                            _stream(x)), "moe_router_logits")
+    return logits
+
+
+def shared_workspace_size(T: int, H: int, I_shared: int, flags: int = 0) -> int:
+    return int(_lib.lib().moe_fp4_shared_workspace_size(T, H, I_shared, flags))
+
+
+def shared_expert(pws: PackedWeights, xq, xs, flags: int = 0, O_shared=None, workspace=None):
+    """The always-active expert (E == 1) on every token's MXFP8 row -> O_shared [T, H] bf16."""
+    T = xq.shape[0]
+    dev = xq.device
+    if O_shared is None:
+        O_shared = torch.empty((T, pws.H), dtype=torch.bfloat16, device=dev)
+    _check_dtype(O_shared, (torch.bfloat16,), "O_shared")
+    if workspace is None:
+        need = shared_workspace_size(T, pws.H, pws.I, flags)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _lib.check(_lib.lib().moe_fp4_shared_expert(
+        ctypes.byref(pws.desc), _ptr(xq), _ptr(xs), T, _ptr(O_shared), _ptr(workspace),
+        workspace.numel(), flags, _stream(xq)), "moe_fp4_shared_expert")
+    return O_shared
+
+
+def combine_shared(O, gates, pair_pos, O_shared, T: int, k: int, H: int, y=None):
+    """combine() plus the shared expert's row, added after the k routed slots."""
+    _check_dtype(O, (torch.bfloat16,), "O")
+    _check_dtype(O_shared, (torch.bfloat16,), "O_shared")
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=O.device)
+    _lib.check(_lib.lib().moe_combine_shared(_ptr(O), _ptr(gates), _ptr(pair_pos), _ptr(O_shared),
+                                             T, k, H, _ptr(y), _stream(O)), "moe_combine_shared")
+    return y
+
+
+def layer_full_workspace_size(T: int, k: int, E: int, H: int, I: int, I_shared: int = 0,
+                              flags: int = 0) -> int:
+    return int(_lib.lib().moe_fp4_layer_full_workspace_size(T, k, E, H, I, I_shared, flags))
+
+
+def layer_forward_full(pw: PackedWeights, pws: PackedWeights | None, router_w: torch.Tensor,
+                       x: torch.Tensor, k: int, flags: int = 0, y=None, workspace=None):
+    """Router GEMM + the layer (+ shared expert when ``pws`` is given), one library call."""
+    _check_dtype(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
+    _check_dtype(router_w, (torch.bfloat16, torch.int16, torch.uint16), "router_w")
+    T, H = x.shape
+    if H != pw.H or tuple(router_w.shape) != (pw.E, pw.H):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, router_w {tuple(router_w.shape)}, "
+                         f"weights E={pw.E} H={pw.H}")
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = layer_full_workspace_size(T, k, pw.E, pw.H, pw.I, pws.I if pws else 0, flags)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _lib.check(_lib.lib().moe_fp4_layer_forward_full(
+        ctypes.byref(pw.desc), ctypes.byref(pws.desc) if pws is not None else None, _ptr(router_w),
+        _ptr(x), T, k, _ptr(y), _ptr(workspace), workspace.numel(), flags, _stream(x)),
+        "moe_fp4_layer_forward_full")
     return y

@@ -1,5 +1,6 @@
-// Gate-weighted combine back to token order: y[t] = sum_j g[t,j] * O[pair_pos[t*k+j]],
-// accumulated in slot order j = 0..k-1 in fp32 with no atomics (a fixed
+// Gate-weighted combine back to token order: y[t] = sum_j g[t,j] * O[pair_pos[t*k+j]]
+// (+ the shared expert's row, when there is one), accumulated in slot order
+// j = 0..k-1 (then the shared row) in fp32 with no atomics (a fixed
 // reduction order, pwwt.cn review section 4.2).  O holds the expert outputs
 // as bf16 (a matrix-multiply output kept at low precision, its sum in fp32:
 // the same review, section 4.1).  Each thread produces four consecutive
@@ -16,7 +17,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __global__ __launch_bounds__(256) void combine_kernel(const uint2* __restrict__ O,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ pair_pos,
-                                                      int k, int H4, float4* __restrict__ y) {
+                                                      const uint2* __restrict__ Os, int k, int H4,
+                                                      float4* __restrict__ y) {
   const int t = blockIdx.x;
   const int c = blockIdx.y * blockDim.x + threadIdx.x;
   if (c >= H4) return;
@@ -44,17 +46,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint2* __restrict__ 
       if (u < n) acc = a;
     }
   }
+  if (Os) {  // the shared expert, weight 1, after the routed slots
+    const uint2 o = Os[(size_t)t * H4 + c];
+    acc.x += bf16_lo(o.x);
+    acc.y += bf16_hi(o.x);
+    acc.z += bf16_lo(o.y);
+    acc.w += bf16_hi(o.y);
+  }
   y[(size_t)t * H4 + c] = acc;
 }
 
 }  // namespace
 
-hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos, int T,
-                          int k, int H, float* y, hipStream_t s) {
+hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos,
+                          const uint16_t* O_shared, int T, int k, int H, float* y, hipStream_t s) {
   const int H4 = H / 4;
   dim3 grid((unsigned)T, (unsigned)((H4 + 255) / 256));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, reinterpret_cast<const uint2*>(O),
-                     gates, pair_pos, k, H4, reinterpret_cast<float4*>(y));
+                     gates, pair_pos, reinterpret_cast<const uint2*>(O_shared), k, H4,
+                     reinterpret_cast<float4*>(y));
   return hipGetLastError();
 }
 

@@ -209,7 +209,10 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
 hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
                                const uint8_t* hs, const int32_t* offsets, int T, int k, uint16_t* O,
                                void* tile_ws, hipStream_t s);
-hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos, int T,
-                          int k, int H, float* y, hipStream_t s);
+hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos,
+                          const uint16_t* O_shared, int T, int k, int H, float* y, hipStream_t s);
+hipError_t launch_router(const uint16_t* x, const uint16_t* wg, int T, int H, int E, float* logits,
+                         hipStream_t s);
+hipError_t launch_identity_route(int T, int32_t* sorted_pair, int32_t* offsets, hipStream_t s);
 
 }  // namespace moe

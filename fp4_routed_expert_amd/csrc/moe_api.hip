@@ -101,6 +101,65 @@ LayerCarve layer_carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
   return c;
 }
 
+// Steps 1-3 of the layer into the carve's buffers: one fused launch for
+// T <= kFrontMaxT, else the stand-alone routing, sort and quantisation.
+moe_status_t run_front(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t H, int32_t E,
+                       int32_t k, uint8_t* ws, const LayerCarve& c, hipStream_t stream) {
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
+  float* gates = reinterpret_cast<float*>(ws + c.gates);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + c.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + c.sorted);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + c.pos);
+  uint8_t* xq = ws + c.xq;
+  uint8_t* xs = ws + c.xs;
+  if (T <= kFrontMaxT)
+    return hip_status(launch_front_small(logits, x_bf16, T, H, E, k, ids, gates, counts, offsets,
+                                         sorted, pos, xq, xs, stream));
+  moe_status_t st = hip_status(launch_route_topk(logits, T, E, k, ids, gates, stream));
+  if (st == MOE_OK)
+    st = hip_status(launch_sort_permute(ids, T, E, k, counts, offsets, sorted, pos, ws + c.sort_ws,
+                                        stream));
+  if (st == MOE_OK) st = hip_status(launch_quant_mxfp8(x_bf16, T, H, xq, xs, stream));
+  return st;
+}
+
+// Workspace of the shared expert: its trivial routing (pair = token), its h
+// and the GEMM stages' workspace.
+struct SharedCarve {
+  size_t sorted, offsets, hq, hs, stage, total;
+};
+
+SharedCarve shared_carve(int32_t T, int32_t H, int32_t Is) {
+  SharedCarve c;
+  c.sorted = 0;
+  c.offsets = align256(c.sorted + (size_t)T * 4);
+  c.hq = align256(c.offsets + 2 * 4);
+  c.hs = align256(c.hq + (size_t)T * Is);
+  c.stage = align256(c.hs + (size_t)T * (Is / 32));
+  c.total = align256(c.stage + stage_ws_bytes(T, 1, 1, H, Is));
+  return c;
+}
+
+// Workspace of the whole layer with router and optional shared expert.
+struct FullCarve {
+  size_t logits, layer, Os, shared, total;
+  LayerCarve lc;
+  SharedCarve sc;
+};
+
+FullCarve full_carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int32_t Is) {
+  FullCarve c;
+  c.lc = layer_carve(T, k, E, H, I);
+  c.logits = 0;
+  c.layer = align256(c.logits + (size_t)T * E * 4);
+  c.Os = align256(c.layer + c.lc.total);
+  c.shared = align256(c.Os + (Is > 0 ? (size_t)T * H * 2 : 0));
+  c.sc = shared_carve(T, H, Is > 0 ? Is : 128);
+  c.total = align256(c.shared + (Is > 0 ? c.sc.total : 0));
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,7 +310,7 @@ moe_status_t moe_combine(const uint16_t* O, const float* topk_gates, const int32
   if (T == 0) return MOE_OK;
   if (!O || !topk_gates || !pair_pos || !y) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(O, 8) || !aligned(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_combine(O, topk_gates, pair_pos, T, k, H, y, stream));
+  return hip_status(launch_combine(O, topk_gates, pair_pos, nullptr, T, k, H, y, stream));
 }
 
 size_t moe_fp4_forward_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
@@ -330,19 +389,133 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w, const uint16_t* x
   int32_t* pos = reinterpret_cast<int32_t*>(ws + c.pos);
   uint8_t* xq = ws + c.xq;
   uint8_t* xs = ws + c.xs;
-  if (T <= kFrontMaxT) {
-    st = hip_status(launch_front_small(logits, x_bf16, T, H, E, k, ids, gates, counts, offsets,
-                                       sorted, pos, xq, xs, stream));
-  } else {
-    st = hip_status(launch_route_topk(logits, T, E, k, ids, gates, stream));
-    if (st == MOE_OK)
-      st = hip_status(launch_sort_permute(ids, T, E, k, counts, offsets, sorted, pos,
-                                          ws + c.sort_ws, stream));
-    if (st == MOE_OK) st = hip_status(launch_quant_mxfp8(x_bf16, T, H, xq, xs, stream));
-  }
+  st = run_front(logits, x_bf16, T, H, E, k, ws, c, stream);
   if (st != MOE_OK) return st;
   return moe_fp4_grouped_forward(w, xq, xs, gates, offsets, sorted, pos, T, k, y, ws + c.fwd,
                                  c.fwd_bytes, flags, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------- router GEMM and shared expert
+extern "C" {
+
+moe_status_t moe_router_logits(const uint16_t* x_bf16, const uint16_t* router_w, int32_t T,
+                               int32_t H, int32_t E, float* logits, hipStream_t stream) {
+  if (T < 0 || H < 1 || E < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 128 != 0 || H > (1 << 20) || E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * E >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !router_w || !logits) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_bf16, 16) || !aligned(router_w, 16) || !aligned(logits, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_router(x_bf16, router_w, T, H, E, logits, stream));
+}
+
+size_t moe_fp4_shared_workspace_size(int32_t T, int32_t H, int32_t I_shared, uint32_t flags) {
+  (void)flags;
+  if (check_tek(T, 1, 1) != MOE_OK || check_hi(H, I_shared) != MOE_OK) return 0;
+  return shared_carve(T, H, I_shared).total;
+}
+
+moe_status_t moe_fp4_shared_expert(const moe_fp4_weights_t* w, const uint8_t* xq, const uint8_t* xs,
+                                   int32_t T, uint16_t* O_shared, void* workspace,
+                                   size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+  moe_status_t st = check_weights(w);
+  if (st != MOE_OK) return st;
+  if (w->E != 1) return MOE_ERR_INVALID_ARGUMENT;
+  st = check_tek(T, 1, 1);
+  if (st != MOE_OK) return st;
+  if (select_path(T, 1, flags) < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!xq || !xs || !O_shared) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(xq, 16) || !aligned(xs, 4) || !aligned(O_shared, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  const SharedCarve c = shared_carve(T, w->H, w->I);
+  if (!workspace || workspace_bytes < c.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + c.sorted);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
+  st = hip_status(launch_identity_route(T, sorted, offsets, stream));
+  if (st != MOE_OK) return st;
+  st = moe_fp4_expert_up(w, xq, xs, offsets, sorted, T, 1, ws + c.hq, ws + c.hs, ws + c.stage,
+                         c.total - c.stage, flags, stream);
+  if (st != MOE_OK) return st;
+  return moe_fp4_expert_down(w, ws + c.hq, ws + c.hs, offsets, T, 1, O_shared, ws + c.stage,
+                             c.total - c.stage, flags, stream);
+}
+
+moe_status_t moe_combine_shared(const uint16_t* O, const float* topk_gates, const int32_t* pair_pos,
+                                const uint16_t* O_shared, int32_t T, int32_t k, int32_t H, float* y,
+                                hipStream_t stream) {
+  if (T < 0 || k < 1 || H < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > kMaxK || H % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!O || !topk_gates || !pair_pos || !O_shared || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(O, 8) || !aligned(O_shared, 8) || !aligned(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_combine(O, topk_gates, pair_pos, O_shared, T, k, H, y, stream));
+}
+
+size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                         int32_t I_shared, uint32_t flags) {
+  (void)flags;
+  if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
+  if (I_shared < 0 || (I_shared > 0 && check_hi(H, I_shared) != MOE_OK)) return 0;
+  return full_carve(T, k, E, H, I, I_shared).total;
+}
+
+moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w,
+                                        const moe_fp4_weights_t* w_shared,
+                                        const uint16_t* router_w, const uint16_t* x_bf16,
+                                        int32_t T, int32_t k, float* y, void* workspace,
+                                        size_t workspace_bytes, uint32_t flags,
+                                        hipStream_t stream) {
+  moe_status_t st = check_weights(w);
+  if (st != MOE_OK) return st;
+  if (w_shared) {
+    st = check_weights(w_shared);
+    if (st != MOE_OK) return st;
+    if (w_shared->E != 1 || w_shared->H != w->H) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  st = check_tek(T, w->E, k);
+  if (st != MOE_OK) return st;
+  if (select_path((int64_t)T * k, w->E, flags) < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)T * w->E >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!router_w || !x_bf16 || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(router_w, 16) || !aligned(x_bf16, 16) || !aligned(y, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t E = w->E, H = w->H, I = w->I, Is = w_shared ? w_shared->I : 0;
+  const FullCarve c = full_carve(T, k, E, H, I, Is);
+  if (!workspace || workspace_bytes < c.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + c.logits);
+  uint8_t* lw = ws + c.layer;
+  const LayerCarve& lc = c.lc;
+  st = hip_status(launch_router(x_bf16, router_w, T, H, E, logits, stream));
+  if (st == MOE_OK) st = run_front(logits, x_bf16, T, H, E, k, lw, lc, stream);
+  if (st != MOE_OK) return st;
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(lw + lc.offsets);
+  const int32_t* sorted = reinterpret_cast<const int32_t*>(lw + lc.sorted);
+  const int32_t* pos = reinterpret_cast<const int32_t*>(lw + lc.pos);
+  const float* gates = reinterpret_cast<const float*>(lw + lc.gates);
+  const uint8_t* xq = lw + lc.xq;
+  const uint8_t* xs = lw + lc.xs;
+  const FwdCarve fc = carve(T, k, E, H, I);
+  uint8_t* fw = lw + lc.fwd;
+  uint16_t* O = reinterpret_cast<uint16_t*>(fw + fc.O);
+  st = moe_fp4_expert_up(w, xq, xs, offsets, sorted, T, k, fw + fc.hq, fw + fc.hs, fw + fc.stage,
+                         fc.total - fc.stage, flags, stream);
+  if (st == MOE_OK)
+    st = moe_fp4_expert_down(w, fw + fc.hq, fw + fc.hs, offsets, T, k, O, fw + fc.stage,
+                             fc.total - fc.stage, flags, stream);
+  if (st != MOE_OK) return st;
+  if (!w_shared) return moe_combine(O, gates, pos, T, k, H, y, stream);
+  uint16_t* Os = reinterpret_cast<uint16_t*>(ws + c.Os);
+  st = moe_fp4_shared_expert(w_shared, xq, xs, T, Os, ws + c.shared, c.sc.total, flags, stream);
+  if (st != MOE_OK) return st;
+  return moe_combine_shared(O, gates, pos, Os, T, k, H, y, stream);
 }
 
 }  // extern "C"

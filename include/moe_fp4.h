@@ -230,6 +230,67 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w /*(host)*/,
                                    void* workspace, size_t workspace_bytes,
                                    uint32_t flags, hipStream_t stream);
 
+/*
+ * Router logits, the gate network's first layer ahead of step 1:
+ * logits[t,e] = sum_h x[t,h] * Wg[e,h], x and Wg bf16, products accumulated
+ * in fp32 by the bf16 matrix cores (the pwwt.cn review, section 4.1, lets the
+ * gate network's first layers run at low precision while the top-k compare
+ * stays fp32).  The summation order is fixed per shape, so results are
+ * reproducible; they differ from an exact sum by at most the fp32 bound
+ * gamma_H * sum_h |x[t,h] * Wg[e,h]|.
+ *   x_bf16 [T, H] bf16 bits, router_w [E, H] bf16 bits (both 16-byte aligned)
+ *   logits [T, E] fp32 (out, overwritten)
+ *   H % 128 == 0, 1 <= E <= 1024
+ */
+moe_status_t moe_router_logits(const uint16_t* x_bf16, const uint16_t* router_w, int32_t T,
+                               int32_t H, int32_t E, float* logits, hipStream_t stream);
+
+/*
+ * Shared expert: one always-active expert of the same FP4 format (E == 1 in
+ * `w`, its own intermediate size w->I) applied to every token's MXFP8 row:
+ * O_shared[t] = W2 * MXFP8(silu(W1 x_t) * (W3 x_t)), bf16 (RNE) as O of the
+ * routed experts.  The DeepSeekMoE layer (pwwt.cn review, section 1.2) pairs
+ * the routed experts with such an expert; it runs the same gate/up and down
+ * kernels as the routed path with the trivial routing pair = token.
+ *   xq [T, H] e4m3, xs [T, H/32] E8M0 (as from moe_quant_mxfp8)
+ *   O_shared [T, H] bf16 bits (out, 16-byte aligned)
+ *   workspace >= moe_fp4_shared_workspace_size(T, H, w->I, flags), 256-aligned
+ *   flags: MOE_FLAG_FORCE_DECODE / MOE_FLAG_FORCE_PREFILL as above
+ */
+size_t moe_fp4_shared_workspace_size(int32_t T, int32_t H, int32_t I_shared, uint32_t flags);
+moe_status_t moe_fp4_shared_expert(const moe_fp4_weights_t* w /*(host), E == 1*/,
+                                   const uint8_t* xq, const uint8_t* xs, int32_t T,
+                                   uint16_t* O_shared, void* workspace, size_t workspace_bytes,
+                                   uint32_t flags, hipStream_t stream);
+
+/*
+ * Combine with a shared expert: moe_combine's sum over the k slots in order,
+ * then + O_shared[t, r] (weight 1), all in fp32.  O_shared [T, H] bf16 bits,
+ * 8-byte aligned; the other arguments as for moe_combine.
+ */
+moe_status_t moe_combine_shared(const uint16_t* O, const float* topk_gates, const int32_t* pair_pos,
+                                const uint16_t* O_shared, int32_t T, int32_t k, int32_t H, float* y,
+                                hipStream_t stream);
+
+/*
+ * The layer from the hidden states: router logits -> steps 1-7 -> (if
+ * w_shared is not NULL) shared expert on the same MXFP8 rows -> combine with
+ * the shared output.  Bitwise identical to moe_router_logits followed by the
+ * single-stage chain (moe_combine_shared in place of moe_combine when there
+ * is a shared expert).  w_shared has E == 1 and the same H as w.
+ *   router_w [E, H] bf16 bits; x_bf16 [T, H] bf16 bits; y [T, H] fp32 (out)
+ *   workspace >= moe_fp4_layer_full_workspace_size(T, k, E, H, I, I_shared,
+ *   flags) bytes, 256-aligned (I_shared = 0 without a shared expert)
+ */
+size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                         int32_t I_shared, uint32_t flags);
+moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/,
+                                        const moe_fp4_weights_t* w_shared /*(host), nullable*/,
+                                        const uint16_t* router_w, const uint16_t* x_bf16,
+                                        int32_t T, int32_t k, float* y, void* workspace,
+                                        size_t workspace_bytes, uint32_t flags,
+                                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 22, names
     so = ctypes.CDLL(_lib.SO_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -140,6 +140,48 @@ def test_layer_forward_argument_errors():
     assert lf(ctypes.byref(d), A, A, 16, 40, A, A, need, 0, NUL) == UNS    # k > 32
     assert lf(ctypes.byref(_desc(version=2)), A, A, 16, 2, A, A, need, 0, NUL) == INV
     assert lf(ctypes.byref(d), NUL, NUL, 0, 2, NUL, NUL, 0, 0, NUL) == 0  # T = 0
+
+
+def test_router_and_shared_argument_errors():
+    rl = L.moe_router_logits
+    assert rl(A, A, 4, 200, 8, A, NUL) == UNS          # H % 128
+    assert rl(A, A, 4, 256, 1025, A, NUL) == UNS       # E > 1024
+    assert rl(A, A, -1, 256, 8, A, NUL) == INV
+    assert rl(A, A, 4, 256, 0, A, NUL) == INV
+    assert rl(MIS, A, 4, 256, 8, A, NUL) == INV        # x not 16-aligned
+    assert rl(A, NUL, 4, 256, 8, A, NUL) == INV
+    assert rl(NUL, NUL, 0, 256, 8, NUL, NUL) == 0      # T = 0
+    d1 = _desc(E=1, I=256)
+    sws = L.moe_fp4_shared_workspace_size(16, 256, 256, 0)
+    # identity routing, h (MXFP8) of the shared intermediate size and the stage workspace
+    assert sws >= 16 * 256 + 16 * 8 + L.moe_fp4_stage_workspace_size(16, 1, 1, 256, 256)
+    se = L.moe_fp4_shared_expert
+    assert se(ctypes.byref(_desc(E=2)), A, A, 16, A, A, sws, 0, NUL) == INV   # E != 1
+    assert se(ctypes.byref(d1), A, A, 16, A, A, sws - 1, 0, NUL) == WSE
+    assert se(ctypes.byref(d1), A, A, 16, A, MIS, sws, 0, NUL) == INV
+    assert se(ctypes.byref(d1), A, A, 16, NUL, A, sws, 0, NUL) == INV
+    assert se(ctypes.byref(d1), A, A, 16, A, A, sws, 3, NUL) == INV           # both paths forced
+    cs = L.moe_combine_shared
+    assert cs(A, A, A, NUL, 4, 2, 256, A, NUL) == INV                        # no shared output
+    assert cs(A, A, A, A, 4, 2, 250, A, NUL) == UNS                          # H % 4
+    assert cs(A, A, A, MIS, 4, 2, 256, A, NUL) == INV                        # not 8-aligned
+    assert cs(A, A, A, A, 4, 2, 256, MIS, NUL) == INV                        # y not 16-aligned
+    d = _desc()
+    full = L.moe_fp4_layer_full_workspace_size
+    n0 = full(16, 2, 8, 256, 128, 0, 0)
+    n1 = full(16, 2, 8, 256, 128, 256, 0)
+    assert n0 >= L.moe_fp4_layer_workspace_size(16, 2, 8, 256, 128, 0) + 16 * 8 * 4   # + logits
+    assert n1 >= n0 + 16 * 256 * 2 + sws                                           # + O_shared
+    assert full(16, 2, 8, 256, 128, 96, 0) == 0                                     # I_shared % 128
+    lf = L.moe_fp4_layer_forward_full
+    assert lf(ctypes.byref(d), None, A, A, 16, 2, A, A, n0 - 1, 0, NUL) == WSE
+    assert lf(ctypes.byref(d), ctypes.byref(d1), A, A, 16, 2, A, A, n0, 0, NUL) == WSE  # needs n1
+    assert lf(ctypes.byref(d), ctypes.byref(_desc(E=1, H=512)), A, A, 16, 2, A, A, n1, 0, NUL) == INV
+    assert lf(ctypes.byref(d), ctypes.byref(_desc(E=2)), A, A, 16, 2, A, A, n1, 0, NUL) == INV
+    assert lf(ctypes.byref(d), None, NUL, A, 16, 2, A, A, n0, 0, NUL) == INV       # no router weights
+    assert lf(ctypes.byref(d), None, MIS, A, 16, 2, A, A, n0, 0, NUL) == INV
+    assert lf(ctypes.byref(d), None, A, A, 16, 9, A, A, n0, 0, NUL) == UNS         # k > E
+    assert lf(ctypes.byref(d), None, NUL, NUL, 0, 2, NUL, NUL, 0, 0, NUL) == 0      # T = 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

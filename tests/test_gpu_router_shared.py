@@ -1,0 +1,200 @@
+"""GPU parity of the router GEMM and the shared expert, through the C ABI.
+
+* Router logits (bf16 x . bf16 Wg, fp32 accumulation on the matrix cores)
+  against the oracle's exact fp64 sums: every logit within the fp32 error
+  bound gamma_n * sum_h |x_h * Wg_h| (n = H plus the few cross-wave adds), on
+  decode shapes (K split over the workgroup's waves), prefill shapes, ragged
+  token and expert counts, and the full-size router of the large prefill
+  workload on sampled tokens.
+* The shared expert: its bf16 output against the oracle's single-expert
+  steps, and bit for bit against the routed stage calls on a one-expert
+  routing (the entry is those kernels with pair = token).
+* The whole layer from hidden states: bit for bit equal to the chain of
+  single-stage calls, and against the oracle's layer with shared expert,
+  routed on the same fp32 logits the GPU produced (so that the integer
+  routing decision is taken on identical values on both sides)."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_routed_expert_amd as moe
+import oracle
+import synth
+from gpu_cases import check_y, get_case, log, sample_tokens, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# Unit roundoff for the bound: the matrix cores' internal rounding of their
+# fp32 adds is not specified as round-to-nearest, so the bound uses 2^-23, the
+# unit roundoff of a directed rounding, which covers either.
+U32 = 2.0 ** -23
+
+
+def _gamma(n: int) -> float:
+    return n * U32 / (1 - n * U32)
+
+
+def _bf16_dev(bits: np.ndarray, dev) -> torch.Tensor:
+    return to_dev(bits.view(np.int16), dev).view(torch.bfloat16)
+
+
+def _check_logits(lg: np.ndarray, x_bits: np.ndarray, wg_bits: np.ndarray, what: str):
+    ref, absum = oracle.router_logits(x_bits, wg_bits)
+    H = x_bits.shape[1]
+    bound = _gamma(H + 4) * absum
+    err = np.abs(lg.astype(np.float64) - ref)
+    worst = float((err / np.maximum(bound, 1e-300)).max())
+    log(f"[{what}] max_err={err.max():.3e} worst err/bound={worst:.3f}")
+    assert np.isfinite(lg).all(), what
+    assert (err <= bound).all(), f"{what}: error beyond the fp32 bound (worst ratio {worst})"
+
+
+ROUTER_SHAPES = [
+    # (T, H, E): decode (K split over 4 waves), ragged, prefill, tiny
+    (1, 128, 8),
+    (8, 4096, 64),
+    (16, 256, 8),
+    (17, 256, 8),
+    (33, 512, 200),
+    (300, 512, 16),
+    (64, 7168, 256),
+    (1000, 1024, 96),
+]
+
+
+@pytest.mark.parametrize("T,H,E", ROUTER_SHAPES, ids=lambda v: str(v))
+def test_router_logits_within_fp32_bound(T, H, E, dev):
+    sh = synth.Shape(T=T, H=H, I=128, E=E, k=1, seed=70 + T % 13)
+    log(f"[router] T{T} H{H} E{E}")
+    x_bits, _ = synth.make_activations(sh)
+    wg_bits = synth.make_router_weights(sh)
+    lg = moe.router_logits(_bf16_dev(x_bits, dev), _bf16_dev(wg_bits, dev))
+    torch.cuda.synchronize()
+    _check_logits(lg.cpu().numpy(), x_bits, wg_bits, f"router T{T} H{H} E{E}")
+
+
+def test_router_logits_full_prefill_size_sampled(dev):
+    """T 4604, H 7168, E 256 (the large prefill workload's router) on sampled tokens."""
+    sh = synth.CONFIGS["c3"]
+    log("[router] c3 sampled")
+    x_bits, _ = synth.make_activations(sh)
+    wg_bits = synth.make_router_weights(sh)
+    lg = moe.router_logits(_bf16_dev(x_bits, dev), _bf16_dev(wg_bits, dev))
+    torch.cuda.synchronize()
+    toks = sample_tokens(sh.T, 48, seed=9)
+    _check_logits(lg.cpu().numpy()[toks], x_bits[toks], wg_bits, "router c3")
+    # repeatable: the same call gives the same bits
+    lg2 = moe.router_logits(_bf16_dev(x_bits, dev), _bf16_dev(wg_bits, dev))
+    torch.cuda.synchronize()
+    assert torch.equal(lg.cpu(), lg2.cpu())
+
+
+def test_router_one_hot_weights_return_the_activations(dev):
+    """Wg rows with a single +1: each logit is one activation, exactly."""
+    T, H, E = 40, 256, 24
+    sh = synth.Shape(T=T, H=H, I=128, E=E, k=1, seed=77)
+    x_bits, _ = synth.make_activations(sh)
+    wg = np.zeros((E, H), dtype=np.uint16)
+    cols = (7 * np.arange(E) + 2) % H
+    wg[np.arange(E), cols] = 0x3F80
+    lg = moe.router_logits(_bf16_dev(x_bits, dev), _bf16_dev(wg, dev)).cpu().numpy()
+    assert np.array_equal(lg, synth.bf16_bits_to_f32(x_bits)[:, cols])
+
+
+def _shared_pw(sh, Is, dev):
+    sw = synth.make_shared_weights(sh, I_shared=Is)
+    pws = moe.prepack_weights(*[to_dev(a, dev) for a in sw])
+    torch.cuda.synchronize()
+    return sw, pws
+
+
+SHARED_CASES = [
+    ("c0", 128, 0),
+    ("c1", 1536, 0),
+    (synth.Shape(T=300, H=512, I=256, E=16, k=4, seed=53), 384, moe.MOE_FLAG_FORCE_PREFILL),
+    (synth.Shape(T=300, H=512, I=256, E=16, k=4, seed=53), 384, moe.MOE_FLAG_FORCE_DECODE),
+]
+
+
+def _sid(v):
+    return v if isinstance(v, str) else f"T{v.T}H{v.H}I{v.I}E{v.E}k{v.k}"
+
+
+@pytest.mark.parametrize("shape,Is,flags", SHARED_CASES,
+                         ids=[f"{_sid(s)}-Is{i}-f{f}" for s, i, f in SHARED_CASES])
+def test_shared_expert_output(shape, Is, flags, dev):
+    c = get_case(shape, dev)
+    sh = c.sh
+    log(f"[shared] {_sid(shape)} Is={Is} flags={flags}")
+    sw, pws = _shared_pw(sh, Is, dev)
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    Os = moe.shared_expert(pws, xq, xs, flags)
+    # the same kernels through the stage calls on a one-expert routing
+    offs = torch.tensor([0, sh.T], dtype=torch.int32, device=dev)
+    ident = torch.arange(sh.T, dtype=torch.int32, device=dev)
+    hq, hs = moe.expert_up(pws, xq, xs, offs, ident, sh.T, 1, flags)
+    O1 = moe.expert_down(pws, hq, hs, offs, sh.T, 1, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(Os.view(torch.int16), O1.view(torch.int16))
+    toks = sample_tokens(sh.T, 16, seed=3)
+    ref = np.empty((toks.size, sh.H))
+    for n, t in enumerate(toks):
+        G, U = oracle.expert_gate_up(c.xq[t], c.xs[t], sw[0][0], sw[1][0], sw[2][0], sw[3][0])
+        _, hq_r, hs_r = oracle.swiglu_requant(G, U)
+        ref[n] = oracle.expert_down(hq_r, hs_r, sw[4][0], sw[5][0])
+    check_y(Os.float().cpu().numpy()[toks], ref, f"shared/{_sid(shape)}/Is{Is}")
+
+
+FULL_CASES = [
+    ("c0", 128, 0, 16),
+    ("c1", 1536, 0, 8),
+    ("c1", 0, 0, 8),                                   # no shared expert
+    (synth.Shape(T=300, H=512, I=256, E=16, k=4, seed=53), 384, moe.MOE_FLAG_FORCE_PREFILL, 24),
+    (synth.Shape(T=40, H=256, I=128, E=8, k=2, seed=54), 256, moe.MOE_FLAG_FORCE_DECODE, 40),
+    ("c3", 2048, 0, 16),
+]
+
+
+@pytest.mark.parametrize("shape,Is,flags,ntok", FULL_CASES,
+                         ids=[f"{_sid(s)}-Is{i}-f{f}" for s, i, f, _ in FULL_CASES])
+def test_layer_full(shape, Is, flags, ntok, dev):
+    c = get_case(shape, dev)
+    sh = c.sh
+    log(f"[full] {_sid(shape)} Is={Is} flags={flags}")
+    wg_bits = synth.make_router_weights(sh)
+    wg = _bf16_dev(wg_bits, dev)
+    sw, pws = _shared_pw(sh, Is, dev) if Is else (None, None)
+    y = moe.layer_forward_full(c.pw, pws, wg, c.x, sh.k, flags)
+    # the chain of single-stage calls
+    lg = moe.router_logits(c.x, wg)
+    if pws is None:
+        y_chain = moe.layer_forward(c.pw, c.x, lg, sh.k, flags)
+    else:
+        ids, gates = moe.route_topk(lg, sh.k)
+        counts, offsets, sp, pp = moe.sort_permute(ids, sh.E)
+        xq, xs = moe.quant_act_mxfp8(c.x)
+        hq, hs = moe.expert_up(c.pw, xq, xs, offsets, sp, sh.T, sh.k, flags)
+        O = moe.expert_down(c.pw, hq, hs, offsets, sh.T, sh.k, flags)
+        Os = moe.shared_expert(pws, xq, xs, flags)
+        y_chain = moe.combine_shared(O, gates, pp, Os, sh.T, sh.k, sh.H)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_chain)
+    lg_np = lg.cpu().numpy()
+    toks = sample_tokens(sh.T, ntok, seed=11)
+    ref = oracle.layer_tokens_shared(c.inp, lg_np, sw, tokens=toks)
+    check_y(y.cpu().numpy()[toks], ref, f"full/{_sid(shape)}/Is{Is}")
+
+
+def test_layer_full_repeatable_and_workspace_poison(dev):
+    c = get_case("c1", dev)
+    sh = c.sh
+    wg = _bf16_dev(synth.make_router_weights(sh), dev)
+    _, pws = _shared_pw(sh, 1536, dev)
+    need = moe.layer_full_workspace_size(sh.T, sh.k, sh.E, sh.H, sh.I, 1536)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev)
+    y1 = moe.layer_forward_full(c.pw, pws, wg, c.x, sh.k, workspace=ws)
+    ws.fill_(0x3C)
+    y2 = torch.full((sh.T, sh.H), float("nan"), device=dev)
+    moe.layer_forward_full(c.pw, pws, wg, c.x, sh.k, y=y2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
