@@ -15,10 +15,17 @@ copies); its algorithmic bytes (decode) or flops (prefill) per launch give
 the roofline fraction against 8 TB/s or the dense FP8 MFMA peak.  The CPU baseline is the
 oracle (a plain fp64 C implementation) on the host's cores, on a bounded
 sample of the same workload.
+
+With --full a step starts from x alone (moe_fp4_layer_forward_full): the router
+logits come from a bf16 GEMM and --n-shared shared experts, packed after the
+routed ones, join every token's slots; the router's HIP-event time (the
+stand-alone call, GEMM plus slice sum) and its roofline against HBM are
+reported beside the gate/up kernel's.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -217,6 +224,10 @@ def main():
                     help="print a markdown summary of rocprofv3 CSV outputs and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic summary of --kernel from two counter runs and exit")
+    ap.add_argument("--full", action="store_true",
+                    help="step = router GEMM + layer + shared expert (moe_fp4_layer_forward_full)")
+    ap.add_argument("--n-shared", type=int, default=1,
+                    help="shared experts with --full (packed after the routed ones, same I)")
     ap.add_argument("--kernel", default="up_decode_kernel")
     ap.add_argument("--workload", default="")
     args = ap.parse_args()
@@ -241,23 +252,38 @@ def main():
     inp = synth.make_inputs(args.config)
     sh = inp.shape
     T, H, I, E, k = sh.T, sh.H, sh.I, sh.E, sh.k
-    P = T * k
+    # --full: ns shared experts packed after the E routed ones, every token's
+    # slots = k routed + ns shared
+    ns = max(args.n_shared, 0) if args.full else 0
+    Ew, kk = E + ns, k + ns
+    P = T * kk
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    canon = [t(getattr(inp, n)) for n in ("w1", "s1", "w3", "s3", "w2", "s2")]
-    packed_bytes = moe.packed_weight_bytes(E, H, I)
+    names = ("w1", "s1", "w3", "s3", "w2", "s2")
+    sws = [synth.make_shared_weights(dataclasses.replace(sh, seed=sh.seed + 1000 * i)) for i in range(ns)]
+    canon = [t(np.concatenate([getattr(inp, n)] + [sw[j] for sw in sws], axis=0)) for j, n in enumerate(names)]
+    del sws
+    packed_bytes = moe.packed_weight_bytes(Ew, H, I)
     copies = args.copies or max(1, min(8, int(np.ceil(2.0e9 / packed_bytes))))
     pws = [moe.prepack_weights(*canon) for _ in range(copies)]
     del canon
     x = t(inp.x.view(np.int16)).view(torch.bfloat16)
     logits = t(inp.logits)
+    if args.full:
+        # router weights, one copy per weight copy
+        wg = [t(synth.make_router_weights(sh).view(np.int16)).view(torch.bfloat16) for _ in range(copies)]
+        r_ws = torch.empty(max(moe.router_workspace_size(T, H, E), 256), dtype=torch.uint8, device=dev)
 
     # all outputs and workspaces allocated once, outside the timed region
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
-    sort_out = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+    ids = torch.empty((T, kk), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, kk), dtype=torch.float32, device=dev)
+    ids[:, k:] = torch.arange(E, Ew, dtype=torch.int32, device=dev)
+    gates[:, k:] = 1.0
+    ids_r = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates_r = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sort_out = (torch.empty(Ew, dtype=torch.int32, device=dev), torch.empty(Ew + 1, dtype=torch.int32, device=dev),
                 torch.empty(P, dtype=torch.int32, device=dev), torch.empty(P, dtype=torch.int32, device=dev))
     from fp4_routed_expert_amd import _lib
-    sort_ws_n = _lib.lib().moe_sort_permute_workspace_size(T, E, k)
+    sort_ws_n = _lib.lib().moe_sort_permute_workspace_size(T, Ew, kk)
     sort_ws = torch.empty(max(sort_ws_n, 256), dtype=torch.uint8, device=dev)
     xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
     xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
@@ -265,26 +291,43 @@ def main():
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=dev)
     O = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
-    stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, k, E, H, I), 256),
+    stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, kk, Ew, H, I), 256),
                            dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-
-    lws = torch.empty(max(moe.layer_workspace_size(T, k, E, H, I, args.flags), 256),
-                      dtype=torch.uint8, device=dev)
+    ev_r = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    if args.full:
+        lws = torch.empty(max(moe.layer_full_workspace_size(T, k, Ew, H, I, ns, args.flags), 256),
+                          dtype=torch.uint8, device=dev)
+    else:
+        lws = torch.empty(max(moe.layer_workspace_size(T, k, E, H, I, args.flags), 256),
+                          dtype=torch.uint8, device=dev)
 
     def step(i):
-        moe.layer_forward(pws[i % copies], x, logits, k, args.flags, y=y, workspace=lws)
+        if args.full:
+            moe.layer_forward_full(pws[i % copies], ns, wg[i % copies], x, k, args.flags, y=y,
+                                   workspace=lws)
+        else:
+            moe.layer_forward(pws[i % copies], x, logits, k, args.flags, y=y, workspace=lws)
 
     def staged_step(i, timed_idx):
         pw = pws[i % copies]
-        moe.route_topk(logits, k, ids, gates)
-        counts, offsets, sp, pp = moe.sort_permute(ids, E, out=sort_out, workspace=sort_ws)
+        if args.full:
+            ev_r[timed_idx][0].record()
+            moe.router_logits(x, wg[i % copies], logits, workspace=r_ws)
+            ev_r[timed_idx][1].record()
+            moe.route_topk(logits, k, ids_r, gates_r)
+            ids[:, :k] = ids_r
+            gates[:, :k] = gates_r
+        else:
+            moe.route_topk(logits, k, ids, gates)
+        counts, offsets, sp, pp = moe.sort_permute(ids, Ew, out=sort_out, workspace=sort_ws)
         moe.quant_act_mxfp8(x, xq, xs)
         ev[timed_idx][0].record()
-        moe.expert_up(pw, xq, xs, offsets, sp, T, k, args.flags, hq=hq, hs=hs, workspace=stage_ws)
+        moe.expert_up(pw, xq, xs, offsets, sp, T, kk, args.flags, hq=hq, hs=hs, workspace=stage_ws)
         ev[timed_idx][1].record()
-        moe.expert_down(pw, hq, hs, offsets, T, k, args.flags, O=O, workspace=stage_ws)
-        moe.combine(O, gates, pp, T, k, H, y=y)
+        moe.expert_down(pw, hq, hs, offsets, T, kk, args.flags, O=O, workspace=stage_ws)
+        moe.combine(O, gates, pp, T, kk, H, y=y)
 
     for i in range(args.warmup):
         step(i)
@@ -296,7 +339,7 @@ def main():
         for c in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                moe.layer_forward(pws[c], x, logits, k, args.flags, y=y, workspace=lws)
+                step(c)
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % copies].replay()
@@ -325,7 +368,7 @@ def main():
     up_gbs = b_up / (up_ms * 1e-3) / 1e9
     flops = 6.0 * H * I * P
     up_flops = 4.0 * H * I * P
-    prefill = args.flags == 2 or (args.flags == 0 and P > 16 * E)
+    prefill = args.flags == 2 or (args.flags == 0 and P > 16 * Ew)
     if prefill:
         achieved = up_flops / (up_ms * 1e-3) / 1e12
         kname = "prefill_gemm_kernel<true>"
@@ -362,6 +405,19 @@ def main():
         "layer_mfma_frac_fp8": flops / (ms_per_step * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
         "roofline": roof,
     }
+    if args.full:
+        # router GEMM: bf16 x and Wg read once, fp32 logits written
+        r_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_r]))
+        r_bytes = T * H * 2 + E * H * 2 + T * E * 4
+        r_gbs = r_bytes / (r_ms * 1e-3) / 1e9
+        line["config"]["workload"] += f" + router GEMM + {ns} shared expert(s)"
+        line["config"]["n_shared"] = ns
+        line["router"] = {"bound": "hbm", "kernel": "router_partial_kernel + router_reduce_kernel (bf16 x . Wg, fp32 logits)",
+                          "achieved": r_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": r_gbs / HBM_PEAK_GBS, "alg_bytes_per_launch": r_bytes,
+                          "alg_flops_per_launch": 2.0 * T * H * E, "avg_launch_us": r_ms * 1e3}
+        line["layer_hbm_tbps"] = (b_layer + E * H * 2) / (ms_per_step * 1e-3) / 1e12
+        line["layer_hbm_frac"] = line["layer_hbm_tbps"] * 1e3 / HBM_PEAK_GBS
     if args.copy_calibration:
         copy_calibration()
     if args.cpu_budget > 0:

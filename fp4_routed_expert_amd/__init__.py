@@ -23,6 +23,7 @@ __all__ = [
     "route_topk", "sort_permute", "quant_act_mxfp8", "prepack_weights", "PackedWeights",
     "expert_up", "expert_down", "combine", "grouped_forward", "moe_layer",
     "forward_workspace_size", "layer_forward", "layer_workspace_size", "router_logits",
+    "router_workspace_size",
     "shared_workspace_size", "shared_expert", "combine_shared", "layer_full_workspace_size",
     "layer_forward_full", "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
 ]
@@ -248,7 +249,11 @@ def moe_layer(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: int, 
 
 
 # ----------------------------------------------------- router and shared expert
-def router_logits(x: torch.Tensor, router_w: torch.Tensor, logits=None):
+def router_workspace_size(T: int, H: int, E: int) -> int:
+    return int(_lib.lib().moe_router_workspace_size(T, H, E))
+
+
+def router_logits(x: torch.Tensor, router_w: torch.Tensor, logits=None, workspace=None):
     """logits [T, E] fp32 = x [T, H] bf16 . router_w [E, H] bf16^T (fp32 accumulation)."""
     _check_dtype(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
     _check_dtype(router_w, (torch.bfloat16, torch.int16, torch.uint16), "router_w")
@@ -259,8 +264,12 @@ def router_logits(x: torch.Tensor, router_w: torch.Tensor, logits=None):
     if logits is None:
         logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
     _check_dtype(logits, (torch.float32,), "logits")
+    if workspace is None:
+        need = router_workspace_size(T, H, E)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _lib.check(_lib.lib().moe_router_logits(_ptr(x), _ptr(router_w), T, H, E, _ptr(logits),
-                                            _stream(x)), "moe_router_logits")
+                                            _ptr(workspace), workspace.numel(), _stream(x)),
+               "moe_router_logits")
     return logits
 
 
@@ -295,28 +304,28 @@ def combine_shared(O, gates, pair_pos, O_shared, T: int, k: int, H: int, y=None)
     return y
 
 
-def layer_full_workspace_size(T: int, k: int, E: int, H: int, I: int, I_shared: int = 0,
+def layer_full_workspace_size(T: int, k: int, E: int, H: int, I: int, n_shared: int = 0,
                               flags: int = 0) -> int:
-    return int(_lib.lib().moe_fp4_layer_full_workspace_size(T, k, E, H, I, I_shared, flags))
+    return int(_lib.lib().moe_fp4_layer_full_workspace_size(T, k, E, H, I, n_shared, flags))
 
 
-def layer_forward_full(pw: PackedWeights, pws: PackedWeights | None, router_w: torch.Tensor,
-                       x: torch.Tensor, k: int, flags: int = 0, y=None, workspace=None):
-    """Router GEMM + the layer (+ shared expert when ``pws`` is given), one library call."""
+def layer_forward_full(pw: PackedWeights, n_shared: int, router_w: torch.Tensor, x: torch.Tensor,
+                       k: int, flags: int = 0, y=None, workspace=None):
+    """Router GEMM + the layer in one library call; the last ``n_shared`` experts of ``pw``
+    are shared (every token, weight 1), the router covers the others."""
     _check_dtype(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
     _check_dtype(router_w, (torch.bfloat16, torch.int16, torch.uint16), "router_w")
     T, H = x.shape
-    if H != pw.H or tuple(router_w.shape) != (pw.E, pw.H):
+    if H != pw.H or tuple(router_w.shape) != (pw.E - n_shared, pw.H):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, router_w {tuple(router_w.shape)}, "
-                         f"weights E={pw.E} H={pw.H}")
+                         f"weights E={pw.E} (n_shared={n_shared}) H={pw.H}")
     dev = x.device
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
     if workspace is None:
-        need = layer_full_workspace_size(T, k, pw.E, pw.H, pw.I, pws.I if pws else 0, flags)
+        need = layer_full_workspace_size(T, k, pw.E, pw.H, pw.I, n_shared, flags)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _lib.check(_lib.lib().moe_fp4_layer_forward_full(
-        ctypes.byref(pw.desc), ctypes.byref(pws.desc) if pws is not None else None, _ptr(router_w),
-        _ptr(x), T, k, _ptr(y), _ptr(workspace), workspace.numel(), flags, _stream(x)),
-        "moe_fp4_layer_forward_full")
+        ctypes.byref(pw.desc), n_shared, _ptr(router_w), _ptr(x), T, k, _ptr(y), _ptr(workspace),
+        workspace.numel(), flags, _stream(x)), "moe_fp4_layer_forward_full")
     return y

@@ -67,12 +67,13 @@ SIGNATURES = {
                                                _U32, _P]),
     "moe_fp4_layer_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _U32]),
     "moe_fp4_layer_forward": (ctypes.c_int, [_WP, _P, _P, _I32, _I32, _P, _P, _SZ, _U32, _P]),
-    "moe_router_logits": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_router_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "moe_router_logits": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "moe_fp4_shared_workspace_size": (_SZ, [_I32, _I32, _I32, _U32]),
     "moe_fp4_shared_expert": (ctypes.c_int, [_WP, _P, _P, _I32, _P, _P, _SZ, _U32, _P]),
     "moe_combine_shared": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
     "moe_fp4_layer_full_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _U32]),
-    "moe_fp4_layer_forward_full": (ctypes.c_int, [_WP, _WP, _P, _P, _I32, _I32, _P, _P, _SZ, _U32,
+    "moe_fp4_layer_forward_full": (ctypes.c_int, [_WP, _I32, _P, _P, _I32, _I32, _P, _P, _SZ, _U32,
                                                   _P]),
 }
 

@@ -179,12 +179,15 @@ struct PackedLayout {
 // Each returns the hipError_t of its launch(es).
 constexpr int kFrontMaxT = 32;  // token counts taken by the fused front kernel
 int route_keys_per_lane(int E);
-hipError_t launch_front_small(const float* logits, const uint16_t* x, int T, int H, int E, int k,
-                              int32_t* ids, float* gates, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_pair, int32_t* pair_pos, uint8_t* xq, uint8_t* xs,
-                              hipStream_t s);
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids,
-                             float* gates, hipStream_t s);
+// The routing launchers read S logit planes T*E floats apart and sum them in
+// plane order (S = 1: plain logits), route over E experts and append ns shared
+// slots (experts E .. E+ns-1, weight 1) after the k routed ones per token.
+hipError_t launch_front_small(const float* logits, int S, const uint16_t* x, int T, int H, int E,
+                              int k, int ns, int32_t* ids, float* gates, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                              uint8_t* xq, uint8_t* xs, hipStream_t s);
+hipError_t launch_route_topk(const float* logits, int S, int T, int E, int k, int ns,
+                             int32_t* ids, float* gates, hipStream_t s);
 size_t sort_workspace_bytes(int T, int E, int k);
 hipError_t launch_sort_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
                                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
@@ -211,8 +214,16 @@ hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, con
                                void* tile_ws, hipStream_t s);
 hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos,
                           const uint16_t* O_shared, int T, int k, int H, float* y, hipStream_t s);
+// partial: router_ws_bytes(T, H, E) bytes of fp32 K-slice partial sums
+// (unused, may be null, when that is 0)
+int router_slices(int T, int H, int E);
+size_t router_ws_bytes(int T, int H, int E);
 hipError_t launch_router(const uint16_t* x, const uint16_t* wg, int T, int H, int E, float* logits,
-                         hipStream_t s);
+                         float* partial, hipStream_t s);
+// Only the GEMM: writes the logits when router_slices() == 1, else the S
+// partial planes in `partial` (for a routing launch that sums them itself).
+hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
+                                  float* logits, float* partial, hipStream_t s);
 hipError_t launch_identity_route(int T, int32_t* sorted_pair, int32_t* offsets, hipStream_t s);
 
 }  // namespace moe

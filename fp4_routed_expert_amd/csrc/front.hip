@@ -17,9 +17,11 @@ constexpr int kFrontThreads = 256;
 constexpr int kFrontWaves = kFrontThreads / 64;
 constexpr int kFrontMaxP = kFrontMaxT * 32;  // k <= 32
 
+// Routing over E experts with k + ns slots per token (ns shared experts with
+// ids E .. E + ns - 1 after the routed slots); the sort covers E + ns experts.
 template <int NK>
 __global__ __launch_bounds__(kFrontThreads) void front_small_kernel(
-    const float* __restrict__ logits, const uint4* __restrict__ x, int T, int E, int k, long n8,
+    LogitSrc L, const uint4* __restrict__ x, int T, int E, int k, int ns, long n8,
     int32_t* __restrict__ ids, float* __restrict__ gates, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_pos, uint2* __restrict__ xq, uint8_t* __restrict__ xs) {
@@ -30,12 +32,13 @@ __global__ __launch_bounds__(kFrontThreads) void front_small_kernel(
   __shared__ SortSmallLds sm;
   __shared__ int sids[kFrontMaxP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ld = k + ns;
   float raw[NK];
   auto fetch = [&](int t) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = lane + 64 * i;
-      raw[i] = (e < E) ? logits[(size_t)t * E + e] : 0.0f;
+      raw[i] = (e < E) ? load_logit(L, (long)t * E + e) : 0.0f;
     }
   };
   if (wave < T) fetch(wave);
@@ -49,29 +52,30 @@ __global__ __launch_bounds__(kFrontThreads) void front_small_kernel(
     if (t + kFrontWaves < T) fetch(t + kFrontWaves);
     int id;
     float g;
-    if (route_topk_token<NK>(r, E, k, lane, &id, &g)) {
-      ids[(size_t)t * k + lane] = id;
-      gates[(size_t)t * k + lane] = g;
-      sids[t * k + lane] = id;
+    if (route_topk_token<NK>(r, E, k, lane, &id, &g) || shared_slot(E, k, ns, lane, &id, &g)) {
+      ids[(size_t)t * ld + lane] = id;
+      gates[(size_t)t * ld + lane] = g;
+      sids[t * ld + lane] = id;
     }
   }
   __syncthreads();
-  sort_small_body(sids, T * k, E, sm, counts, offsets, sorted_pair, pair_pos);
+  sort_small_body(sids, T * ld, E + ns, sm, counts, offsets, sorted_pair, pair_pos);
 }
 
 }  // namespace
 
-hipError_t launch_front_small(const float* logits, const uint16_t* x, int T, int H, int E, int k,
-                              int32_t* ids, float* gates, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_pair, int32_t* pair_pos, uint8_t* xq, uint8_t* xs,
-                              hipStream_t s) {
-  if (T < 1 || T > kFrontMaxT || k > 32) return hipErrorInvalidValue;
+hipError_t launch_front_small(const float* logits, int S, const uint16_t* x, int T, int H, int E,
+                              int k, int ns, int32_t* ids, float* gates, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                              uint8_t* xq, uint8_t* xs, hipStream_t s) {
+  if (T < 1 || T > kFrontMaxT || k + ns > 32 || E + ns > kMaxE) return hipErrorInvalidValue;
+  const LogitSrc L{logits, (long)T * E, S};
   const long n8 = (long)T * H / 8;
   const dim3 grid((unsigned)(1 + (n8 + kFrontThreads - 1) / kFrontThreads)), block(kFrontThreads);
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint2* qv = reinterpret_cast<uint2*>(xq);
 #define MOE_FRONT(nk)                                                                             \
-  hipLaunchKernelGGL(front_small_kernel<nk>, grid, block, 0, s, logits, xv, T, E, k, n8, ids,     \
+  hipLaunchKernelGGL(front_small_kernel<nk>, grid, block, 0, s, L, xv, T, E, k, ns, n8, ids,     \
                      gates, counts, offsets, sorted_pair, pair_pos, qv, xs)
   switch (route_keys_per_lane(E)) {
     case 1: MOE_FRONT(1); break;

@@ -102,9 +102,13 @@ LayerCarve layer_carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
 }
 
 // Steps 1-3 of the layer into the carve's buffers: one fused launch for
-// T <= kFrontMaxT, else the stand-alone routing, sort and quantisation.
-moe_status_t run_front(const float* logits, const uint16_t* x_bf16, int32_t T, int32_t H, int32_t E,
-                       int32_t k, uint8_t* ws, const LayerCarve& c, hipStream_t stream) {
+// T <= kFrontMaxT, else the stand-alone routing, sort and quantisation.  The
+// logits are S planes summed in order (S = 1: plain logits); routing is over
+// E experts, with ns shared experts (E .. E+ns-1, weight 1) appended as slots
+// k .. k+ns-1 of every token; c is the carve for k + ns slots and E + ns experts.
+moe_status_t run_front(const float* logits, int S, const uint16_t* x_bf16, int32_t T, int32_t H,
+                       int32_t E, int32_t k, int32_t ns, uint8_t* ws, const LayerCarve& c,
+                       hipStream_t stream) {
   int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
   float* gates = reinterpret_cast<float*>(ws + c.gates);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + c.counts);
@@ -114,12 +118,12 @@ moe_status_t run_front(const float* logits, const uint16_t* x_bf16, int32_t T, i
   uint8_t* xq = ws + c.xq;
   uint8_t* xs = ws + c.xs;
   if (T <= kFrontMaxT)
-    return hip_status(launch_front_small(logits, x_bf16, T, H, E, k, ids, gates, counts, offsets,
-                                         sorted, pos, xq, xs, stream));
-  moe_status_t st = hip_status(launch_route_topk(logits, T, E, k, ids, gates, stream));
+    return hip_status(launch_front_small(logits, S, x_bf16, T, H, E, k, ns, ids, gates, counts,
+                                         offsets, sorted, pos, xq, xs, stream));
+  moe_status_t st = hip_status(launch_route_topk(logits, S, T, E, k, ns, ids, gates, stream));
   if (st == MOE_OK)
-    st = hip_status(launch_sort_permute(ids, T, E, k, counts, offsets, sorted, pos, ws + c.sort_ws,
-                                        stream));
+    st = hip_status(launch_sort_permute(ids, T, E + ns, k + ns, counts, offsets, sorted, pos,
+                                        ws + c.sort_ws, stream));
   if (st == MOE_OK) st = hip_status(launch_quant_mxfp8(x_bf16, T, H, xq, xs, stream));
   return st;
 }
@@ -141,22 +145,21 @@ SharedCarve shared_carve(int32_t T, int32_t H, int32_t Is) {
   return c;
 }
 
-// Workspace of the whole layer with router and optional shared expert.
+// Workspace of the layer from hidden states: the router's output (its S
+// K-slice planes, or the logits when S == 1) and the layer's own carve for
+// k + ns slots over E experts (E = routed + shared).
 struct FullCarve {
-  size_t logits, layer, Os, shared, total;
+  size_t rout, layer, total;
   LayerCarve lc;
-  SharedCarve sc;
 };
 
-FullCarve full_carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int32_t Is) {
+FullCarve full_carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int32_t ns) {
   FullCarve c;
-  c.lc = layer_carve(T, k, E, H, I);
-  c.logits = 0;
-  c.layer = align256(c.logits + (size_t)T * E * 4);
-  c.Os = align256(c.layer + c.lc.total);
-  c.shared = align256(c.Os + (Is > 0 ? (size_t)T * H * 2 : 0));
-  c.sc = shared_carve(T, H, Is > 0 ? Is : 128);
-  c.total = align256(c.shared + (Is > 0 ? c.sc.total : 0));
+  const int32_t Er = E - ns;
+  c.rout = 0;
+  c.layer = align256(c.rout + (size_t)router_slices(T, H, Er) * T * Er * 4);
+  c.lc = layer_carve(T, k + ns, E, H, I);
+  c.total = align256(c.layer + c.lc.total);
   return c;
 }
 
@@ -185,7 +188,7 @@ moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k
   if (!logits || !topk_ids || !topk_gates) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_gates, 4))
     return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_route_topk(logits, T, E, k, topk_ids, topk_gates, stream));
+  return hip_status(launch_route_topk(logits, 1, T, E, k, 0, topk_ids, topk_gates, stream));
 }
 
 size_t moe_sort_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
@@ -381,17 +384,13 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w, const uint16_t* x
   if (!workspace || workspace_bytes < c.total) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int32_t* ids = reinterpret_cast<int32_t*>(ws + c.ids);
-  float* gates = reinterpret_cast<float*>(ws + c.gates);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + c.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + c.sorted);
-  int32_t* pos = reinterpret_cast<int32_t*>(ws + c.pos);
-  uint8_t* xq = ws + c.xq;
-  uint8_t* xs = ws + c.xs;
-  st = run_front(logits, x_bf16, T, H, E, k, ws, c, stream);
+  st = run_front(logits, 1, x_bf16, T, H, E, k, 0, ws, c, stream);
   if (st != MOE_OK) return st;
-  return moe_fp4_grouped_forward(w, xq, xs, gates, offsets, sorted, pos, T, k, y, ws + c.fwd,
+  return moe_fp4_grouped_forward(w, ws + c.xq, ws + c.xs,
+                                 reinterpret_cast<const float*>(ws + c.gates),
+                                 reinterpret_cast<const int32_t*>(ws + c.offsets),
+                                 reinterpret_cast<const int32_t*>(ws + c.sorted),
+                                 reinterpret_cast<const int32_t*>(ws + c.pos), T, k, y, ws + c.fwd,
                                  c.fwd_bytes, flags, stream);
 }
 
@@ -400,16 +399,33 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w, const uint16_t* x
 // ------------------------------------------- router GEMM and shared expert
 extern "C" {
 
-moe_status_t moe_router_logits(const uint16_t* x_bf16, const uint16_t* router_w, int32_t T,
-                               int32_t H, int32_t E, float* logits, hipStream_t stream) {
+static moe_status_t check_router(int32_t T, int32_t H, int32_t E) {
   if (T < 0 || H < 1 || E < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (H % 128 != 0 || H > (1 << 20) || E > kMaxE) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)T * E >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * E * router_slices(T > 0 ? T : 1, H, E) >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_router_workspace_size(int32_t T, int32_t H, int32_t E) {
+  if (check_router(T, H, E) != MOE_OK || T == 0) return 0;
+  return router_ws_bytes(T, H, E);
+}
+
+moe_status_t moe_router_logits(const uint16_t* x_bf16, const uint16_t* router_w, int32_t T,
+                               int32_t H, int32_t E, float* logits, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  moe_status_t st = check_router(T, H, E);
+  if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !router_w || !logits) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x_bf16, 16) || !aligned(router_w, 16) || !aligned(logits, 4))
     return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_router(x_bf16, router_w, T, H, E, logits, stream));
+  const size_t need = router_ws_bytes(T, H, E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(
+      launch_router(x_bf16, router_w, T, H, E, logits, static_cast<float*>(workspace), stream));
 }
 
 size_t moe_fp4_shared_workspace_size(int32_t T, int32_t H, int32_t I_shared, uint32_t flags) {
@@ -456,66 +472,56 @@ moe_status_t moe_combine_shared(const uint16_t* O, const float* topk_gates, cons
   return hip_status(launch_combine(O, topk_gates, pair_pos, O_shared, T, k, H, y, stream));
 }
 
-size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
-                                         int32_t I_shared, uint32_t flags) {
-  (void)flags;
-  if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
-  if (I_shared < 0 || (I_shared > 0 && check_hi(H, I_shared) != MOE_OK)) return 0;
-  return full_carve(T, k, E, H, I, I_shared).total;
+static moe_status_t check_full(int32_t T, int32_t k, int32_t E, int32_t H, int32_t ns) {
+  if (ns < 0 || ns >= E) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_tek(T, E - ns, k);
+  if (st != MOE_OK) return st;
+  if (k + ns > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * (k + ns) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  return check_router(T, H, E - ns);
 }
 
-moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w,
-                                        const moe_fp4_weights_t* w_shared,
+size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                         int32_t n_shared, uint32_t flags) {
+  (void)flags;
+  if (E < 1 || E > kMaxE || check_hi(H, I) != MOE_OK) return 0;
+  if (check_full(T, k, E, H, n_shared) != MOE_OK) return 0;
+  return full_carve(T, k, E, H, I, n_shared).total;
+}
+
+moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w, int32_t n_shared,
                                         const uint16_t* router_w, const uint16_t* x_bf16,
                                         int32_t T, int32_t k, float* y, void* workspace,
                                         size_t workspace_bytes, uint32_t flags,
                                         hipStream_t stream) {
   moe_status_t st = check_weights(w);
   if (st != MOE_OK) return st;
-  if (w_shared) {
-    st = check_weights(w_shared);
-    if (st != MOE_OK) return st;
-    if (w_shared->E != 1 || w_shared->H != w->H) return MOE_ERR_INVALID_ARGUMENT;
-  }
-  st = check_tek(T, w->E, k);
+  st = check_full(T, k, w->E, w->H, n_shared);
   if (st != MOE_OK) return st;
-  if (select_path((int64_t)T * k, w->E, flags) < 0) return MOE_ERR_INVALID_ARGUMENT;
-  if ((int64_t)T * w->E >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  const int32_t E = w->E, H = w->H, I = w->I, ns = n_shared, Er = E - ns, kk = k + ns;
+  if (select_path((int64_t)T * kk, E, flags) < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   if (!router_w || !x_bf16 || !y) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(router_w, 16) || !aligned(x_bf16, 16) || !aligned(y, 16))
     return MOE_ERR_INVALID_ARGUMENT;
-  const int32_t E = w->E, H = w->H, I = w->I, Is = w_shared ? w_shared->I : 0;
-  const FullCarve c = full_carve(T, k, E, H, I, Is);
+  const FullCarve c = full_carve(T, k, E, H, I, ns);
   if (!workspace || workspace_bytes < c.total) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* logits = reinterpret_cast<float*>(ws + c.logits);
+  float* rout = reinterpret_cast<float*>(ws + c.rout);
+  const int S = router_slices(T, H, Er);
   uint8_t* lw = ws + c.layer;
   const LayerCarve& lc = c.lc;
-  st = hip_status(launch_router(x_bf16, router_w, T, H, E, logits, stream));
-  if (st == MOE_OK) st = run_front(logits, x_bf16, T, H, E, k, lw, lc, stream);
+  // the router GEMM leaves S planes; the routing launch sums them in plane order
+  st = hip_status(launch_router_partials(x_bf16, router_w, T, H, Er, rout, rout, stream));
+  if (st == MOE_OK) st = run_front(rout, S, x_bf16, T, H, Er, k, ns, lw, lc, stream);
   if (st != MOE_OK) return st;
-  const int32_t* offsets = reinterpret_cast<const int32_t*>(lw + lc.offsets);
-  const int32_t* sorted = reinterpret_cast<const int32_t*>(lw + lc.sorted);
-  const int32_t* pos = reinterpret_cast<const int32_t*>(lw + lc.pos);
-  const float* gates = reinterpret_cast<const float*>(lw + lc.gates);
-  const uint8_t* xq = lw + lc.xq;
-  const uint8_t* xs = lw + lc.xs;
-  const FwdCarve fc = carve(T, k, E, H, I);
-  uint8_t* fw = lw + lc.fwd;
-  uint16_t* O = reinterpret_cast<uint16_t*>(fw + fc.O);
-  st = moe_fp4_expert_up(w, xq, xs, offsets, sorted, T, k, fw + fc.hq, fw + fc.hs, fw + fc.stage,
-                         fc.total - fc.stage, flags, stream);
-  if (st == MOE_OK)
-    st = moe_fp4_expert_down(w, fw + fc.hq, fw + fc.hs, offsets, T, k, O, fw + fc.stage,
-                             fc.total - fc.stage, flags, stream);
-  if (st != MOE_OK) return st;
-  if (!w_shared) return moe_combine(O, gates, pos, T, k, H, y, stream);
-  uint16_t* Os = reinterpret_cast<uint16_t*>(ws + c.Os);
-  st = moe_fp4_shared_expert(w_shared, xq, xs, T, Os, ws + c.shared, c.sc.total, flags, stream);
-  if (st != MOE_OK) return st;
-  return moe_combine_shared(O, gates, pos, Os, T, k, H, y, stream);
+  return moe_fp4_grouped_forward(w, lw + lc.xq, lw + lc.xs,
+                                 reinterpret_cast<const float*>(lw + lc.gates),
+                                 reinterpret_cast<const int32_t*>(lw + lc.offsets),
+                                 reinterpret_cast<const int32_t*>(lw + lc.sorted),
+                                 reinterpret_cast<const int32_t*>(lw + lc.pos), T, kk, y,
+                                 lw + lc.fwd, lc.fwd_bytes, flags, stream);
 }
 
 }  // extern "C"

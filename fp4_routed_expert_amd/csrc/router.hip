@@ -4,116 +4,138 @@
 // at low precision while the top-k compare stays fp32 (pwwt.cn review,
 // section 4.1, the operator classes and the row "MoE routing top-k").
 //
-// v_mfma_f32_16x16x16bf16_1k: lane l supplies 4 bf16 of row l%16 (A) or
-// column l%16 (B) for K slots 4*(l/16) .. +3.  The dot product does not care
-// which K element sits in which slot as long as A and B agree, so each lane
-// loads 8 consecutive bf16 (16 bytes) at K offset k0 + 8*(l/16) of its row and
-// feeds the low 4 to one MFMA and the high 4 to a second: two MFMAs cover 32 K.
+// v_mfma_f32_16x16x32_bf16: lane l supplies 8 bf16 of row l%16 (A) or column
+// l%16 (B); A and B use the same lane-to-K assignment, so each lane loads the
+// 8 consecutive bf16 (16 bytes) at K offset k0 + 8*(l/16) of its row and one
+// instruction covers 32 K.
 //
-// A wave owns 16 tokens x 64 experts (4 output tiles, 16 fp32 per lane).  With
-// more than 16 tokens the 4 waves of a workgroup take 4 token tiles of one
-// 64-expert tile; with at most 16 tokens (decode) they split K instead and add
-// their partial sums through LDS in wave order, so the result does not depend
-// on timing.  Workgroups are laid out XCD by XCD: the expert tiles of one token
-// tile run on one XCD and share its L2 copy of the x rows.
-#include "common.h"
+// The GEMM is skinny (E <= 1024 columns, K = H up to 7168 and more), so the
+// work is split along K as well as over output tiles, deterministically:
+//   * a wave item is (token tile of 16*TM rows, 64-expert group, K slice s);
+//     a wave accumulates its 16*TM x 64 block over its slice and writes it to
+//     partial[s] (or straight to the logits when there is a single slice);
+//   * a second pass adds the S partial blocks of every logit in slice order.
+// The slice count S is a function of (T, H, E) only, so the summation order,
+// hence every bit of the result, is fixed per shape.  Workgroup b works on
+// slice b % S and lands on XCD b % 8: with S a multiple of 4 each XCD reads
+// a fixed set of K columns of Wg into its L2 and reuses them for every token
+// tile, and the four waves of a workgroup share their x rows in L1.
+#include "stages.h"
 
 namespace moe {
 namespace {
 
-typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ v4s lo4(uint4 v) {
-  return v4s{(short)(v.x & 0xFFFF), (short)(v.x >> 16), (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
-}
-__device__ __forceinline__ v4s hi4(uint4 v) {
-  return v4s{(short)(v.z & 0xFFFF), (short)(v.z >> 16), (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
+__device__ __forceinline__ v8bf as_bf8(uint4 v) { return __builtin_bit_cast(v8bf, v); }
+
+// Chunks of 32 K in flight per wave (a chunk is TM + 4 16-byte loads per lane).
+template <int TM>
+constexpr int ring_depth() {
+  return TM == 1 ? 3 : 3;
 }
 
-// One 32-K chunk of a wave: A (16 token rows) and B (4 x 16 expert rows).
+template <int TM>
 struct Chunk {
-  uint4 a;
+  uint4 a[TM];
   uint4 b[4];
 };
 
-__device__ __forceinline__ void load_chunk(Chunk& c, const uint16_t* __restrict__ xrow,
+template <int TM>
+__device__ __forceinline__ void load_chunk(Chunk<TM>& c, const uint16_t* const (&xrow)[TM],
                                            const uint16_t* const (&wrow)[4], int k) {
-  c.a = *reinterpret_cast<const uint4*>(xrow + k);
+#pragma unroll
+  for (int m = 0; m < TM; ++m) c.a[m] = *reinterpret_cast<const uint4*>(xrow[m] + k);
 #pragma unroll
   for (int n = 0; n < 4; ++n) c.b[n] = *reinterpret_cast<const uint4*>(wrow[n] + k);
 }
 
-__device__ __forceinline__ void mma_chunk(const Chunk& c, v4f (&acc)[4]) {
+template <int TM>
+__device__ __forceinline__ void mma_chunk(const Chunk<TM>& c, v4f (&acc)[TM][4]) {
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo4(c.a), lo4(c.b[n]), acc[n], 0, 0, 0);
-    acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi4(c.a), hi4(c.b[n]), acc[n], 0, 0, 0);
-  }
+  for (int m = 0; m < TM; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(c.a[m]), as_bf8(c.b[n]), acc[m][n],
+                                                          0, 0, 0);
 }
 
-// KW waves split K (KW = 4: one token tile per workgroup; KW = 1: 4 token tiles).
-template <int KW>
-__global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
-                                                     const uint16_t* __restrict__ wg, int T, int H,
-                                                     int E, float* __restrict__ logits) {
-  constexpr int kMW = 4 / KW;  // token tiles per workgroup
+// out: partial[S][T][E] fp32 (S > 1) or the logits [T][E] (S == 1)
+template <int TM>
+__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ wg, int T,
+                                                             int H, int E, int S,
+                                                             float* __restrict__ out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int NT = (T + 16 * kMW - 1) / (16 * kMW), NE = (E + 63) / 64;
-  const int W = NT * NE;
-  // XCD-major item order: workgroup b runs on XCD b % 8
-  const int per = (W + 7) >> 3;
-  const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if ((blockIdx.x >> 3) >= (unsigned)per || item >= W) return;
-  const int tt = item / NE, et = item % NE;
-  const int t0 = 16 * (kMW * tt + (KW == 1 ? wave : 0));
-  const int e0 = 64 * et;
+  const int NT = (T + 16 * TM - 1) / (16 * TM), NE = (E + 63) / 64;
+  const int s = (int)(blockIdx.x % (unsigned)S);
+  const int q = (int)(blockIdx.x / (unsigned)S) * 4 + wave;  // (token tile, expert group)
+  if (q >= NT * NE) return;                                   // whole wave leaves: no barriers
+  const int tt = q / NE, eg = q % NE;
+  const int t0 = 16 * TM * tt, e0 = 64 * eg;
   const int g = lane >> 4, r = lane & 15;
-  // this lane's token row and expert rows (clamped: rows past T or E are
-  // computed from the last valid row and never stored)
-  const uint16_t* xrow = x + (size_t)min(t0 + r, T - 1) * H + 8 * g;
+  // this lane's rows (clamped: rows past T or E are computed from the last
+  // valid row and never stored)
+  const uint16_t* xrow[TM];
   const uint16_t* wrow[4];
+#pragma unroll
+  for (int m = 0; m < TM; ++m) xrow[m] = x + (size_t)min(t0 + 16 * m + r, T - 1) * H + 8 * g;
 #pragma unroll
   for (int n = 0; n < 4; ++n) wrow[n] = wg + (size_t)min(e0 + 16 * n + r, E - 1) * H + 8 * g;
 
   const int nchunk = H / 32;
-  const int c0 = (KW == 1) ? 0 : (wave * nchunk) / KW;
-  const int c1 = (KW == 1) ? nchunk : ((wave + 1) * nchunk) / KW;
-  v4f acc[4];
+  const int c0 = (int)(((long)s * nchunk) / S), c1 = (int)(((long)(s + 1) * nchunk) / S);
+  v4f acc[TM][4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
-  // two chunks in flight: the next chunk loads while this one multiplies
-  Chunk cur, nxt;
-  if (c0 < c1) load_chunk(cur, xrow, wrow, 32 * c0);
-  for (int c = c0; c < c1; ++c) {
-    if (c + 1 < c1) load_chunk(nxt, xrow, wrow, 32 * (c + 1));
-    mma_chunk(cur, acc);
-    cur = nxt;
-  }
+  for (int m = 0; m < TM; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  if (KW > 1) {
-    __shared__ v4f red[KW][4][64];
+  // Ring of kRing chunks: chunk c + kRing - 1 loads while chunk c multiplies.
+  // The steady-state loop has no branches (loads past the slice re-read its
+  // last chunk and are never used), so the compiler's wait counts let the
+  // younger loads stay in flight; the last chunks run in a plain tail loop.
+  constexpr int kRing = ring_depth<TM>();
+  Chunk<TM> ring[kRing];
+  const int last = c1 - 1;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) red[wave][n][lane] = acc[n];
-    __syncthreads();
-    if (wave != 0) return;
+  for (int i = 0; i < kRing - 1; ++i) load_chunk(ring[i], xrow, wrow, 32 * min(c0 + i, last));
+  int c = c0;
+  for (; c + kRing <= c1; c += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      load_chunk(ring[(i + kRing - 1) % kRing], xrow, wrow, 32 * min(c + i + kRing - 1, last));
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this chunk's MFMAs
+      mma_chunk(ring[i], acc);
+    }
+  }
+  // c1 - c < kRing chunks left; chunk c sits in ring[0], c + 1 in ring[1], ...
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i)
+    if (c + i < c1) mma_chunk(ring[i], acc);
+
+  // lane holds rows 4*(lane>>4)+v of each token tile, column lane&15 of each expert tile
+  float* o = out + (S > 1 ? (size_t)s * T * E : 0);
+#pragma unroll
+  for (int m = 0; m < TM; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      v4f s = red[0][n][lane];
+      const int e = e0 + 16 * n + r;
 #pragma unroll
-      for (int w = 1; w < KW; ++w) s += red[w][n][lane];
-      acc[n] = s;
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 16 * m + 4 * g + v;
+        if (t < T && e < E) o[(size_t)t * E + e] = acc[m][n][v];
+      }
     }
-  }
-  // lane holds rows 4*(lane>>4)+v of the token tile, column lane&15 of each expert tile
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int e = e0 + 16 * n + r;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = t0 + 4 * g + v;
-      if (t < T && e < E) logits[(size_t)t * E + e] = acc[n][v];
-    }
-  }
+}
+
+// logits[i] = ((partial[0][i] + partial[1][i]) + ...) + partial[S-1][i], the
+// same order in which the routing kernels sum the partials they read directly
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, long n,
+                                                            int S, float* __restrict__ logits) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  logits[i] = slice_sum(part, n, S, i);
 }
 
 // The trivial routing of an always-selected expert: pair p = token p (k = 1),
@@ -128,7 +150,36 @@ __global__ __launch_bounds__(256) void identity_route_kernel(int T, int32_t* __r
   }
 }
 
+int router_tm(int T) { return T <= 16 ? 1 : 4; }
+
 }  // namespace
+
+// Number of K slices, rounded up to a multiple of 4 (each XCD then works on
+// a fixed set of K ranges) and capped so that every slice has at least 4
+// chunks of 32.  Decode (one token tile): slices of about 16 chunks, a wave's
+// whole slice in a few round trips while the partial planes stay few for the
+// routing launch to add.  Larger T: none while the output tiles alone give
+// the chip about 1024 waves, otherwise enough slices for that.
+int router_slices(int T, int H, int E) {
+  const int tm = router_tm(T);
+  const int nchunk = H / 32;
+  long want;
+  if (tm == 1) {
+    want = (nchunk + 15) / 16;
+  } else {
+    const long base = (long)((T + 16 * tm - 1) / (16 * tm)) * ((E + 63) / 64);
+    want = (1024 + base - 1) / base;
+  }
+  if (want <= 1) return 1;
+  const int smax = nchunk / 4 > 1 ? nchunk / 4 : 1;
+  const long s4 = (want + 3) / 4 * 4;
+  return (int)(s4 < smax ? s4 : smax);
+}
+
+size_t router_ws_bytes(int T, int H, int E) {
+  const int S = router_slices(T, H, E);
+  return S > 1 ? (size_t)S * T * E * sizeof(float) : 0;
+}
 
 hipError_t launch_identity_route(int T, int32_t* sorted_pair, int32_t* offsets, hipStream_t s) {
   hipLaunchKernelGGL(identity_route_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, T,
@@ -136,16 +187,28 @@ hipError_t launch_identity_route(int T, int32_t* sorted_pair, int32_t* offsets, 
   return hipGetLastError();
 }
 
-hipError_t launch_router(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
-                         float* logits, hipStream_t s) {
-  const int kw = T <= 16 ? 4 : 1;
-  const int mw = 4 / kw;
-  const long W = (long)((T + 16 * mw - 1) / (16 * mw)) * ((E + 63) / 64);
-  const unsigned nb = (unsigned)((W + 7) / 8 * 8);
-  if (kw == 4)
-    hipLaunchKernelGGL(router_kernel<4>, dim3(nb), dim3(256), 0, s, x, wg, T, H, E, logits);
+hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
+                                  float* logits, float* partial, hipStream_t s) {
+  const int tm = router_tm(T);
+  const int S = router_slices(T, H, E);
+  const long items = (long)((T + 16 * tm - 1) / (16 * tm)) * ((E + 63) / 64);
+  const unsigned nb = (unsigned)(S * ((items + 3) / 4));
+  float* out = S > 1 ? partial : logits;
+  if (tm == 1)
+    hipLaunchKernelGGL(router_partial_kernel<1>, dim3(nb), dim3(256), 0, s, x, wg, T, H, E, S, out);
   else
-    hipLaunchKernelGGL(router_kernel<1>, dim3(nb), dim3(256), 0, s, x, wg, T, H, E, logits);
+    hipLaunchKernelGGL(router_partial_kernel<4>, dim3(nb), dim3(256), 0, s, x, wg, T, H, E, S, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* wg, int T, int H, int E, float* logits,
+                         float* partial, hipStream_t s) {
+  hipError_t e = launch_router_partials(x, wg, T, H, E, logits, partial, s);
+  const int S = router_slices(T, H, E);
+  if (e != hipSuccess || S == 1) return e;
+  const long n = (long)T * E;
+  hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     partial, n, S, logits);
   return hipGetLastError();
 }
 

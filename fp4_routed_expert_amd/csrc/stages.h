@@ -40,6 +40,35 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Where a routing kernel reads its logits: S fp32 planes S_stride floats
+// apart whose element-wise sum, taken in plane order, is the logit (S = 1:
+// the logits themselves; S > 1: the K-slice partial sums of the router GEMM).
+struct LogitSrc {
+  const float* p;
+  long sstride;
+  int S;
+};
+
+// (((p[0] + p[1]) + p[2]) + ...) over the S planes at element i, loads issued
+// eight at a time.
+__device__ __forceinline__ float slice_sum(const float* __restrict__ p, long sstride, int S,
+                                           long i) {
+  float a = p[i];
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (s0 + u < S) ? p[(size_t)(s0 + u) * sstride + i] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) a += v[u];
+  }
+  return a;
+}
+
+__device__ __forceinline__ float load_logit(const LogitSrc& L, long i) {
+  return L.S == 1 ? L.p[i] : slice_sum(L.p, L.sstride, L.S, i);
+}
+
 // Logits of one token held by one wave as 64-bit keys: high word the ordered
 // score, low word E-1-e, so that the unsigned order is (score descending,
 // expert index ascending) and every key is distinct.  Absent experts hold 0,
@@ -50,13 +79,29 @@ struct RouteKeys {
 };
 
 template <int NK>
-__device__ __forceinline__ void load_route_keys(RouteKeys<NK>& r, const float* __restrict__ row,
+__device__ __forceinline__ void load_route_keys(RouteKeys<NK>& r, const LogitSrc& L, long row0,
                                                 int E, int lane) {
+  float raw[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     const int e = lane + 64 * i;
-    r.key[i] = (e < E) ? (((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+    raw[i] = (e < E) ? load_logit(L, row0 + e) : 0.0f;
   }
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int e = lane + 64 * i;
+    r.key[i] = (e < E) ? (((uint64_t)ordered_bits(raw[i]) << 32) | (uint32_t)(E - 1 - e)) : 0ull;
+  }
+}
+
+// Slot j of a token's k + ns slots: lanes j < k take the routed top-k (from
+// route_topk_token), lanes k <= j < k + ns the shared experts E + (j - k),
+// always selected, with weight 1.  Returns false on lanes past the last slot.
+__device__ __forceinline__ bool shared_slot(int E, int k, int ns, int lane, int* id, float* gate) {
+  if (lane < k || lane >= k + ns) return false;
+  *id = E + (lane - k);
+  *gate = 1.0f;
+  return true;
 }
 
 // Top-k of one token (pwwt.cn review, section 4.1 table row "MoE routing

@@ -237,21 +237,29 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w /*(host)*/,
  * gate network's first layers run at low precision while the top-k compare
  * stays fp32).  The summation order is fixed per shape, so results are
  * reproducible; they differ from an exact sum by at most the fp32 bound
- * gamma_H * sum_h |x[t,h] * Wg[e,h]|.
+ * gamma_H * sum_h |x[t,h] * Wg[e,h]| (gamma_n = n*u/(1-n*u), u the fp32
+ * unit roundoff).  The sum over H is split into a shape-dependent number of
+ * K slices whose fp32 partial sums are added in slice order in `workspace`.
  *   x_bf16 [T, H] bf16 bits, router_w [E, H] bf16 bits (both 16-byte aligned)
  *   logits [T, E] fp32 (out, overwritten)
+ *   workspace >= moe_router_workspace_size(T, H, E) bytes, 256-aligned (may
+ *   be NULL when that size is 0)
  *   H % 128 == 0, 1 <= E <= 1024
  */
+size_t moe_router_workspace_size(int32_t T, int32_t H, int32_t E);
 moe_status_t moe_router_logits(const uint16_t* x_bf16, const uint16_t* router_w, int32_t T,
-                               int32_t H, int32_t E, float* logits, hipStream_t stream);
+                               int32_t H, int32_t E, float* logits, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Shared expert: one always-active expert of the same FP4 format (E == 1 in
  * `w`, its own intermediate size w->I) applied to every token's MXFP8 row:
  * O_shared[t] = W2 * MXFP8(silu(W1 x_t) * (W3 x_t)), bf16 (RNE) as O of the
  * routed experts.  The DeepSeekMoE layer (pwwt.cn review, section 1.2) pairs
- * the routed experts with such an expert; it runs the same gate/up and down
- * kernels as the routed path with the trivial routing pair = token.
+ * the routed experts with such an expert; this stage call takes one of any
+ * intermediate size and runs the same gate/up and down kernels as the routed
+ * path with the trivial routing pair = token (shared experts of the routed
+ * intermediate size run inside the routed GEMMs: moe_fp4_layer_forward_full).
  *   xq [T, H] e4m3, xs [T, H/32] E8M0 (as from moe_quant_mxfp8)
  *   O_shared [T, H] bf16 bits (out, 16-byte aligned)
  *   workspace >= moe_fp4_shared_workspace_size(T, H, w->I, flags), 256-aligned
@@ -273,19 +281,29 @@ moe_status_t moe_combine_shared(const uint16_t* O, const float* topk_gates, cons
                                 hipStream_t stream);
 
 /*
- * The layer from the hidden states: router logits -> steps 1-7 -> (if
- * w_shared is not NULL) shared expert on the same MXFP8 rows -> combine with
- * the shared output.  Bitwise identical to moe_router_logits followed by the
- * single-stage chain (moe_combine_shared in place of moe_combine when there
- * is a shared expert).  w_shared has E == 1 and the same H as w.
- *   router_w [E, H] bf16 bits; x_bf16 [T, H] bf16 bits; y [T, H] fp32 (out)
- *   workspace >= moe_fp4_layer_full_workspace_size(T, k, E, H, I, I_shared,
- *   flags) bytes, 256-aligned (I_shared = 0 without a shared expert)
+ * The layer from hidden states, with shared experts: router logits ->
+ * top-k routing over the routed experts -> every token also sent to each
+ * shared expert with weight 1 -> sort/permute -> MXFP8(x) -> expert GEMMs ->
+ * combine.  The DeepSeekMoE layer (pwwt.cn review, section 1.2) pairs routed
+ * experts with always-active shared ones; here they are the LAST n_shared
+ * experts of `w` (same format and intermediate size as the routed ones: a
+ * shared FFN of intermediate n*I is n such experts), so they run inside the
+ * routed grouped GEMMs as one more group of T rows each.  Token t's slots are
+ * its k routed experts in rank order, then the shared experts in index order
+ * with gate 1.0, so y_t = sum_j g_j O_j + sum_s O_shared_s, added in that
+ * order in fp32.  The router's K-slice partial sums are read by the routing
+ * launch directly (summed in the same order as moe_router_logits), so the
+ * logits equal moe_router_logits' bit for bit.
+ *   w: E = E_routed + n_shared experts (0 <= n_shared < E); router_w
+ *   [E_routed, H] bf16 bits; x_bf16 [T, H] bf16 bits; y [T, H] fp32 (out)
+ *   1 <= k <= E_routed, k + n_shared <= 32
+ *   workspace >= moe_fp4_layer_full_workspace_size(T, k, E, H, I, n_shared,
+ *   flags) bytes, 256-aligned
+ *   flags: MOE_FLAG_FORCE_DECODE / MOE_FLAG_FORCE_PREFILL as above
  */
 size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
-                                         int32_t I_shared, uint32_t flags);
-moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/,
-                                        const moe_fp4_weights_t* w_shared /*(host), nullable*/,
+                                         int32_t n_shared, uint32_t flags);
+moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/, int32_t n_shared,
                                         const uint16_t* router_w, const uint16_t* x_bf16,
                                         int32_t T, int32_t k, float* y, void* workspace,
                                         size_t workspace_bytes, uint32_t flags,

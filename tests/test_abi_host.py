@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     so = ctypes.CDLL(_lib.SO_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -144,13 +144,21 @@ def test_layer_forward_argument_errors():
 
 def test_router_and_shared_argument_errors():
     rl = L.moe_router_logits
-    assert rl(A, A, 4, 200, 8, A, NUL) == UNS          # H % 128
-    assert rl(A, A, 4, 256, 1025, A, NUL) == UNS       # E > 1024
-    assert rl(A, A, -1, 256, 8, A, NUL) == INV
-    assert rl(A, A, 4, 256, 0, A, NUL) == INV
-    assert rl(MIS, A, 4, 256, 8, A, NUL) == INV        # x not 16-aligned
-    assert rl(A, NUL, 4, 256, 8, A, NUL) == INV
-    assert rl(NUL, NUL, 0, 256, 8, NUL, NUL) == 0      # T = 0
+    rws = L.moe_router_workspace_size(8, 4096, 64)
+    # decode: the K range is split into slices whose fp32 partial sums live in the workspace
+    assert rws >= 2 * 8 * 64 * 4 and rws % (8 * 64 * 4) == 0
+    assert L.moe_router_workspace_size(16384, 7168, 256) == 0   # enough output tiles: no split
+    assert L.moe_router_workspace_size(8, 200, 64) == 0         # unsupported H
+    assert rl(A, A, 4, 200, 8, A, A, 1 << 20, NUL) == UNS          # H % 128
+    assert rl(A, A, 4, 256, 1025, A, A, 1 << 20, NUL) == UNS       # E > 1024
+    assert rl(A, A, -1, 256, 8, A, A, 1 << 20, NUL) == INV
+    assert rl(A, A, 4, 256, 0, A, A, 1 << 20, NUL) == INV
+    assert rl(MIS, A, 4, 256, 8, A, A, 1 << 20, NUL) == INV        # x not 16-aligned
+    assert rl(A, NUL, 4, 256, 8, A, A, 1 << 20, NUL) == INV
+    assert rl(A, A, 8, 4096, 64, A, A, rws - 1, NUL) == WSE
+    assert rl(A, A, 8, 4096, 64, A, NUL, rws, NUL) == WSE
+    assert rl(A, A, 8, 4096, 64, A, MIS, rws, NUL) == INV
+    assert rl(NUL, NUL, 0, 256, 8, NUL, NUL, 0, NUL) == 0          # T = 0
     d1 = _desc(E=1, I=256)
     sws = L.moe_fp4_shared_workspace_size(16, 256, 256, 0)
     # identity routing, h (MXFP8) of the shared intermediate size and the stage workspace
@@ -166,22 +174,28 @@ def test_router_and_shared_argument_errors():
     assert cs(A, A, A, A, 4, 2, 250, A, NUL) == UNS                          # H % 4
     assert cs(A, A, A, MIS, 4, 2, 256, A, NUL) == INV                        # not 8-aligned
     assert cs(A, A, A, A, 4, 2, 256, MIS, NUL) == INV                        # y not 16-aligned
-    d = _desc()
+    d = _desc()                    # 8 experts
     full = L.moe_fp4_layer_full_workspace_size
     n0 = full(16, 2, 8, 256, 128, 0, 0)
-    n1 = full(16, 2, 8, 256, 128, 256, 0)
-    assert n0 >= L.moe_fp4_layer_workspace_size(16, 2, 8, 256, 128, 0) + 16 * 8 * 4   # + logits
-    assert n1 >= n0 + 16 * 256 * 2 + sws                                           # + O_shared
-    assert full(16, 2, 8, 256, 128, 96, 0) == 0                                     # I_shared % 128
+    n1 = full(16, 2, 8, 256, 128, 1, 0)   # 7 routed + 1 shared: 3 slots per token
+    assert n0 >= (L.moe_fp4_layer_workspace_size(16, 2, 8, 256, 128, 0)
+                  + L.moe_router_workspace_size(16, 256, 8))                  # + router planes
+    assert n1 >= L.moe_fp4_layer_workspace_size(16, 3, 8, 256, 128, 0)
+    assert full(16, 2, 8, 256, 128, 8, 0) == 0          # no routed expert left
+    assert full(16, 2, 8, 256, 128, -1, 0) == 0
+    assert full(16, 8, 8, 256, 128, 1, 0) == 0          # k > routed experts
+    assert full(16, 30, 64, 256, 128, 3, 0) == 0        # k + n_shared > 32
     lf = L.moe_fp4_layer_forward_full
-    assert lf(ctypes.byref(d), None, A, A, 16, 2, A, A, n0 - 1, 0, NUL) == WSE
-    assert lf(ctypes.byref(d), ctypes.byref(d1), A, A, 16, 2, A, A, n0, 0, NUL) == WSE  # needs n1
-    assert lf(ctypes.byref(d), ctypes.byref(_desc(E=1, H=512)), A, A, 16, 2, A, A, n1, 0, NUL) == INV
-    assert lf(ctypes.byref(d), ctypes.byref(_desc(E=2)), A, A, 16, 2, A, A, n1, 0, NUL) == INV
-    assert lf(ctypes.byref(d), None, NUL, A, 16, 2, A, A, n0, 0, NUL) == INV       # no router weights
-    assert lf(ctypes.byref(d), None, MIS, A, 16, 2, A, A, n0, 0, NUL) == INV
-    assert lf(ctypes.byref(d), None, A, A, 16, 9, A, A, n0, 0, NUL) == UNS         # k > E
-    assert lf(ctypes.byref(d), None, NUL, NUL, 0, 2, NUL, NUL, 0, 0, NUL) == 0      # T = 0
+    assert lf(ctypes.byref(d), 0, A, A, 16, 2, A, A, n0 - 1, 0, NUL) == WSE
+    assert n1 > n0
+    assert lf(ctypes.byref(d), 1, A, A, 16, 2, A, A, n1 - 1, 0, NUL) == WSE   # the shared slot's rows
+    assert lf(ctypes.byref(d), 8, A, A, 16, 2, A, A, n1, 0, NUL) == INV       # n_shared >= E
+    assert lf(ctypes.byref(d), -1, A, A, 16, 2, A, A, n1, 0, NUL) == INV
+    assert lf(ctypes.byref(d), 1, A, A, 16, 8, A, A, n1, 0, NUL) == UNS       # k > E - n_shared
+    assert lf(ctypes.byref(d), 0, NUL, A, 16, 2, A, A, n0, 0, NUL) == INV     # no router weights
+    assert lf(ctypes.byref(d), 0, MIS, A, 16, 2, A, A, n0, 0, NUL) == INV
+    assert lf(ctypes.byref(d), 0, A, A, 16, 2, A, A, n0, 3, NUL) == INV       # both paths forced
+    assert lf(ctypes.byref(d), 0, NUL, NUL, 0, 2, NUL, NUL, 0, 0, NUL) == 0   # T = 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

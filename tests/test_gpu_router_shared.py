@@ -2,17 +2,21 @@
 
 * Router logits (bf16 x . bf16 Wg, fp32 accumulation on the matrix cores)
   against the oracle's exact fp64 sums: every logit within the fp32 error
-  bound gamma_n * sum_h |x_h * Wg_h| (n = H plus the few cross-wave adds), on
-  decode shapes (K split over the workgroup's waves), prefill shapes, ragged
-  token and expert counts, and the full-size router of the large prefill
-  workload on sampled tokens.
-* The shared expert: its bf16 output against the oracle's single-expert
-  steps, and bit for bit against the routed stage calls on a one-expert
-  routing (the entry is those kernels with pair = token).
-* The whole layer from hidden states: bit for bit equal to the chain of
-  single-stage calls, and against the oracle's layer with shared expert,
-  routed on the same fp32 logits the GPU produced (so that the integer
-  routing decision is taken on identical values on both sides)."""
+  bound gamma_n * sum_h |x_h * Wg_h| (n = H plus a few), on decode shapes
+  (many K slices), prefill shapes, ragged token and expert counts, shapes
+  with no K split, and the full-size router of the large prefill workload on
+  sampled tokens.
+* The shared expert stage call: its bf16 output against the oracle's
+  single-expert steps, and bit for bit against the routed stage calls on a
+  one-expert routing (the entry is those kernels with pair = token).
+* The whole layer from hidden states, with shared experts packed after the
+  routed ones: bit for bit equal to the chain of single-stage calls on the
+  same slots, to the separately packed shared expert's stage call, and within
+  tolerance of the oracle's layer with shared expert, routed on the same fp32
+  logits the GPU produced (so that the integer routing decision is taken on
+  identical values on both sides)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -50,15 +54,17 @@ def _check_logits(lg: np.ndarray, x_bits: np.ndarray, wg_bits: np.ndarray, what:
 
 
 ROUTER_SHAPES = [
-    # (T, H, E): decode (K split over 4 waves), ragged, prefill, tiny
-    (1, 128, 8),
-    (8, 4096, 64),
-    (16, 256, 8),
-    (17, 256, 8),
-    (33, 512, 200),
-    (300, 512, 16),
-    (64, 7168, 256),
-    (1000, 1024, 96),
+    # (T, H, E) with the number of K slices the library picks in brackets:
+    (1, 128, 8),         # tiny, one K slice of 4 chunks [1]
+    (8, 4096, 64),       # decode [8]
+    (16, 256, 8),        # largest one-tile token count [1]
+    (17, 256, 8),        # 64-row token tiles, 17 valid rows [2]
+    (33, 512, 200),      # ragged tokens and experts [4]
+    (300, 512, 16),      # [4]
+    (64, 7168, 256),     # decode batch [56]
+    (16, 7168, 256),     # decode, wide [16]
+    (1000, 1024, 96),    # [8]
+    (4096, 256, 1024),   # enough output tiles: no K split [1]
 ]
 
 
@@ -145,56 +151,92 @@ def test_shared_expert_output(shape, Is, flags, dev):
     check_y(Os.float().cpu().numpy()[toks], ref, f"shared/{_sid(shape)}/Is{Is}")
 
 
+def _with_shared(c, sws, dev):
+    """Packed weights of the routed experts followed by the shared ones (E_r + ns experts)."""
+    names = ("w1", "s1", "w3", "s3", "w2", "s2")
+    cat = [np.concatenate([getattr(c.inp, n)] + [sw[i] for sw in sws], axis=0) for i, n in enumerate(names)]
+    pw = moe.prepack_weights(*[to_dev(a, dev) for a in cat])
+    torch.cuda.synchronize()
+    return pw
+
+
+def _shared_list(sh, ns):
+    return [synth.make_shared_weights(sh if i == 0 else dataclasses.replace(sh, seed=sh.seed + 1000 * i))
+            for i in range(ns)]
+
+
+def _oracle_shared_rows(c, sw, toks):
+    out = np.empty((toks.size, c.sh.H))
+    for n, t in enumerate(toks):
+        G, U = oracle.expert_gate_up(c.xq[t], c.xs[t], sw[0][0], sw[1][0], sw[2][0], sw[3][0])
+        _, hq_r, hs_r = oracle.swiglu_requant(G, U)
+        out[n] = oracle.expert_down(hq_r, hs_r, sw[4][0], sw[5][0])
+    return out
+
+
 FULL_CASES = [
-    ("c0", 128, 0, 16),
-    ("c1", 1536, 0, 8),
-    ("c1", 0, 0, 8),                                   # no shared expert
-    (synth.Shape(T=300, H=512, I=256, E=16, k=4, seed=53), 384, moe.MOE_FLAG_FORCE_PREFILL, 24),
-    (synth.Shape(T=40, H=256, I=128, E=8, k=2, seed=54), 256, moe.MOE_FLAG_FORCE_DECODE, 40),
-    ("c3", 2048, 0, 16),
+    # (shape, shared experts, flags, sampled tokens)
+    ("c0", 1, 0, 16),
+    ("c1", 1, 0, 8),
+    ("c1", 0, 0, 8),
+    (synth.Shape(T=300, H=512, I=256, E=16, k=4, seed=53), 1, moe.MOE_FLAG_FORCE_PREFILL, 24),
+    (synth.Shape(T=300, H=512, I=256, E=16, k=4, seed=53), 2, moe.MOE_FLAG_FORCE_DECODE, 24),
+    (synth.Shape(T=40, H=256, I=128, E=8, k=2, seed=54), 1, moe.MOE_FLAG_FORCE_DECODE, 40),
+    ("c3", 1, 0, 16),
 ]
 
 
-@pytest.mark.parametrize("shape,Is,flags,ntok", FULL_CASES,
-                         ids=[f"{_sid(s)}-Is{i}-f{f}" for s, i, f, _ in FULL_CASES])
-def test_layer_full(shape, Is, flags, ntok, dev):
+@pytest.mark.parametrize("shape,ns,flags,ntok", FULL_CASES,
+                         ids=[f"{_sid(s)}-ns{n}-f{f}" for s, n, f, _ in FULL_CASES])
+def test_layer_full(shape, ns, flags, ntok, dev):
     c = get_case(shape, dev)
     sh = c.sh
-    log(f"[full] {_sid(shape)} Is={Is} flags={flags}")
-    wg_bits = synth.make_router_weights(sh)
-    wg = _bf16_dev(wg_bits, dev)
-    sw, pws = _shared_pw(sh, Is, dev) if Is else (None, None)
-    y = moe.layer_forward_full(c.pw, pws, wg, c.x, sh.k, flags)
-    # the chain of single-stage calls
+    log(f"[full] {_sid(shape)} ns={ns} flags={flags}")
+    wg = _bf16_dev(synth.make_router_weights(sh), dev)
+    sws = _shared_list(sh, ns)
+    pw = _with_shared(c, sws, dev) if ns else c.pw
+    y = moe.layer_forward_full(pw, ns, wg, c.x, sh.k, flags)
+    # the chain of single-stage calls on the same slots: routed top-k, then the shared ids
     lg = moe.router_logits(c.x, wg)
-    if pws is None:
-        y_chain = moe.layer_forward(c.pw, c.x, lg, sh.k, flags)
-    else:
-        ids, gates = moe.route_topk(lg, sh.k)
-        counts, offsets, sp, pp = moe.sort_permute(ids, sh.E)
-        xq, xs = moe.quant_act_mxfp8(c.x)
-        hq, hs = moe.expert_up(c.pw, xq, xs, offsets, sp, sh.T, sh.k, flags)
-        O = moe.expert_down(c.pw, hq, hs, offsets, sh.T, sh.k, flags)
-        Os = moe.shared_expert(pws, xq, xs, flags)
-        y_chain = moe.combine_shared(O, gates, pp, Os, sh.T, sh.k, sh.H)
+    ids, gates = moe.route_topk(lg, sh.k)
+    if ns:
+        sh_ids = torch.arange(sh.E, sh.E + ns, dtype=torch.int32, device=dev).expand(sh.T, ns)
+        ids = torch.cat([ids, sh_ids], dim=1).contiguous()
+        gates = torch.cat([gates, torch.ones((sh.T, ns), device=dev)], dim=1).contiguous()
+    counts, offsets, sp, pp = moe.sort_permute(ids, sh.E + ns)
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    y_chain = moe.grouped_forward(pw, xq, xs, gates, offsets, sp, pp, flags)
     torch.cuda.synchronize()
     assert torch.equal(y, y_chain)
+    if ns == 1 and flags:
+        # the separately packed shared expert through its own stage call: same kernels, same bits
+        pws = moe.prepack_weights(*[to_dev(a, dev) for a in sws[0]])
+        ids_r, gates_r = moe.route_topk(lg, sh.k)
+        _, off_r, sp_r, pp_r = moe.sort_permute(ids_r, sh.E)
+        hq, hs = moe.expert_up(c.pw, xq, xs, off_r, sp_r, sh.T, sh.k, flags)
+        O = moe.expert_down(c.pw, hq, hs, off_r, sh.T, sh.k, flags)
+        Os = moe.shared_expert(pws, xq, xs, flags)
+        y_sep = moe.combine_shared(O, gates_r, pp_r, Os, sh.T, sh.k, sh.H)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_sep)
     lg_np = lg.cpu().numpy()
     toks = sample_tokens(sh.T, ntok, seed=11)
-    ref = oracle.layer_tokens_shared(c.inp, lg_np, sw, tokens=toks)
-    check_y(y.cpu().numpy()[toks], ref, f"full/{_sid(shape)}/Is{Is}")
+    ref = oracle.layer_tokens_shared(c.inp, lg_np, sws[0] if ns else None, tokens=toks).astype(np.float64)
+    for sw in sws[1:]:
+        ref += _oracle_shared_rows(c, sw, toks)
+    check_y(y.cpu().numpy()[toks], ref, f"full/{_sid(shape)}/ns{ns}")
 
 
 def test_layer_full_repeatable_and_workspace_poison(dev):
     c = get_case("c1", dev)
     sh = c.sh
     wg = _bf16_dev(synth.make_router_weights(sh), dev)
-    _, pws = _shared_pw(sh, 1536, dev)
-    need = moe.layer_full_workspace_size(sh.T, sh.k, sh.E, sh.H, sh.I, 1536)
+    pw = _with_shared(c, _shared_list(sh, 1), dev)
+    need = moe.layer_full_workspace_size(sh.T, sh.k, sh.E + 1, sh.H, sh.I, 1)
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev)
-    y1 = moe.layer_forward_full(c.pw, pws, wg, c.x, sh.k, workspace=ws)
+    y1 = moe.layer_forward_full(pw, 1, wg, c.x, sh.k, workspace=ws)
     ws.fill_(0x3C)
     y2 = torch.full((sh.T, sh.H), float("nan"), device=dev)
-    moe.layer_forward_full(c.pw, pws, wg, c.x, sh.k, y=y2, workspace=ws)
+    moe.layer_forward_full(pw, 1, wg, c.x, sh.k, y=y2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
