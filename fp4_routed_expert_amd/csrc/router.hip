@@ -129,6 +129,139 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __r
     }
 }
 
+// ------------------------------------------------ LDS-tiled GEMM, large T
+// A workgroup (4 waves, 2 x 2) owns a 128-token x 128-expert tile and one K
+// slice; per stage of 64 K it stages 16 KB of x rows and 16 KB of Wg rows in
+// LDS (each row's eight 16-byte granules XOR-swizzled by row & 7 so that the
+// fragment reads of 16 consecutive rows spread over the banks), double
+// buffered: the next stage's global loads are in flight while the current
+// stage's 32 MFMAs per wave run, and one barrier per stage separates the
+// buffers' reuse.  Rows past T or E are clamped to the last valid row and
+// never stored.
+constexpr int kTB = 128;          // tile rows (tokens) = tile columns (experts)
+constexpr int kTK = 64;           // K per stage
+constexpr int kTStage = 2 * kTB * kTK * 2;  // bytes of one stage (x and Wg)
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+struct TileLoad {
+  v4u a[4], b[4];
+};
+
+__device__ __forceinline__ int swz(int row, int q) { return row * 128 + ((q ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ void tile_gload(TileLoad& r, const uint16_t* const (&ga)[4],
+                                           const uint16_t* const (&gb)[4], int st) {
+  const int k = st * kTK;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.a[j] = *reinterpret_cast<const v4u*>(ga[j] + k);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.b[j] = *reinterpret_cast<const v4u*>(gb[j] + k);
+}
+
+__device__ __forceinline__ void tile_lstore(const TileLoad& r, uint8_t* buf, int lr, int lq) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<v4u*>(buf + swz(32 * j + lr, lq)) = r.a[j];
+    *reinterpret_cast<v4u*>(buf + kTB * 128 + swz(32 * j + lr, lq)) = r.b[j];
+  }
+}
+
+// One stage's 2 x 16 MFMAs of a wave from the LDS buffer `cur`.
+__device__ __forceinline__ void tile_compute(v4f (&acc)[4][4], const uint8_t* cur, int abase,
+                                             int bbase, int fo0, int fo1) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int fo = kk ? fo1 : fo0;
+    v8bf a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v8bf*>(cur + abase + 16 * 128 * i + fo);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v8bf*>(cur + bbase + 16 * 128 * j + fo);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wg, int T,
+                                                           int H, int E, int S,
+                                                           float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int NTm = (T + kTB - 1) / kTB, NTn = (E + kTB - 1) / kTB;
+  // block -> (slice, token tile, expert tile); slice-minor so that each XCD
+  // (block % 8) keeps a fixed set of K slices of Wg in its L2
+  const int s = (int)(blockIdx.x % (unsigned)S);
+  const int tile = (int)(blockIdx.x / (unsigned)S);
+  const int tm = tile / NTn, tn = tile % NTn;
+  if (tm >= NTm) return;  // uniform per block: before any barrier
+  const int m0 = tm * kTB, n0 = tn * kTB;
+  const int nst = H / kTK;
+  const int st0 = (int)(((long)s * nst) / S), st1 = (int)(((long)(s + 1) * nst) / S);
+
+  // this thread's four x rows and four Wg rows (32 rows apart) and granule
+  const int lr = tid >> 3, lq = tid & 7;
+  const uint16_t* ga[4];
+  const uint16_t* gb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ga[j] = x + (size_t)min(m0 + 32 * j + lr, T - 1) * H + 8 * lq;
+    gb[j] = wg + (size_t)min(n0 + 32 * j + lr, E - 1) * H + 8 * lq;
+  }
+  // fragment offsets: row (16-row block base) + lane & 15, granule 4 kk + lane >> 4
+  const int fr = lane & 15, fg = lane >> 4;
+  const int fo0 = swz(fr, fg), fo1 = swz(fr, 4 + fg);
+  const int abase = (64 * wm) * 128, bbase = kTB * 128 + (64 * wn) * 128;
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Two register sets: stage st + 2 loads while stage st multiplies and stage
+  // st + 1 (loaded one stage earlier) goes from registers to the idle LDS
+  // buffer.  Loads past the slice re-read its last stage and are never used.
+  const int last = st1 - 1;
+  TileLoad p, q;
+  tile_gload(p, ga, gb, st0);
+  tile_gload(q, ga, gb, min(st0 + 1, last));
+  tile_lstore(p, lds, lr, lq);
+  __syncthreads();
+  uint8_t* const buf0 = lds;
+  uint8_t* const buf1 = lds + kTStage;
+  int st = st0;
+  for (; st + 2 <= st1; st += 2) {
+    tile_gload(p, ga, gb, min(st + 2, last));
+    tile_compute(acc, buf0, abase, bbase, fo0, fo1);
+    tile_lstore(q, buf1, lr, lq);
+    __syncthreads();
+    tile_gload(q, ga, gb, min(st + 3, last));
+    tile_compute(acc, buf1, abase, bbase, fo0, fo1);
+    tile_lstore(p, buf0, lr, lq);
+    __syncthreads();
+  }
+  if (st < st1) tile_compute(acc, buf0, abase, bbase, fo0, fo1);  // odd count: last stage in buf0
+
+  float* o = out + (S > 1 ? (size_t)s * T * E : 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = n0 + 64 * wn + 16 * j + fr;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = m0 + 64 * wm + 16 * i + 4 * fg + v;
+        if (t < T && e < E) o[(size_t)t * E + e] = acc[i][j][v];
+      }
+    }
+}
+
 // logits[i] = ((partial[0][i] + partial[1][i]) + ...) + partial[S-1][i], the
 // same order in which the routing kernels sum the partials they read directly
 __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, long n,
@@ -152,15 +285,26 @@ __global__ __launch_bounds__(256) void identity_route_kernel(int T, int32_t* __r
 
 int router_tm(int T) { return T <= 16 ? 1 : 4; }
 
+// Token counts from which the LDS-tiled kernel runs the GEMM.
+constexpr int kTiledMinT = 128;
+
 }  // namespace
 
-// Number of K slices, rounded up to a multiple of 4 (each XCD then works on
-// a fixed set of K ranges) and capped so that every slice has at least 4
-// chunks of 32.  Decode (one token tile): slices of about 16 chunks, a wave's
-// whole slice in a few round trips while the partial planes stay few for the
-// routing launch to add.  Larger T: none while the output tiles alone give
-// the chip about 1024 waves, otherwise enough slices for that.
+// Number of K slices, capped so that every slice keeps at least 4 steps of
+// its kernel's K unit.  Decode (one token tile of 16): slices of about 16
+// chunks of 32, rounded up to a multiple of 4 (each XCD then works on a fixed
+// set of K ranges), a wave's whole slice in a few round trips while the
+// partial planes stay few for the routing launch to add.  Medium T: none
+// while the output tiles give the chip about 1024 waves, else enough slices
+// for that (multiple of 4).  Tiled (large T): as many slices as keep the
+// workgroups within one per compute unit (256).
 int router_slices(int T, int H, int E) {
+  if (T >= kTiledMinT) {
+    const long tiles = (long)((T + kTB - 1) / kTB) * ((E + kTB - 1) / kTB);
+    const long want = 256 / tiles > 1 ? 256 / tiles : 1;
+    const int smax = H / kTK / 4 > 1 ? H / kTK / 4 : 1;
+    return (int)(want < smax ? want : smax);
+  }
   const int tm = router_tm(T);
   const int nchunk = H / 32;
   long want;
@@ -189,8 +333,14 @@ hipError_t launch_identity_route(int T, int32_t* sorted_pair, int32_t* offsets, 
 
 hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
                                   float* logits, float* partial, hipStream_t s) {
-  const int tm = router_tm(T);
   const int S = router_slices(T, H, E);
+  if (T >= kTiledMinT) {
+    const long tiles = (long)((T + kTB - 1) / kTB) * ((E + kTB - 1) / kTB);
+    hipLaunchKernelGGL(router_tiled_kernel, dim3((unsigned)(tiles * S)), dim3(256), 2 * kTStage, s,
+                       x, wg, T, H, E, S, S > 1 ? partial : logits);
+    return hipGetLastError();
+  }
+  const int tm = router_tm(T);
   const long items = (long)((T + 16 * tm - 1) / (16 * tm)) * ((E + 63) / 64);
   const unsigned nb = (unsigned)(S * ((items + 3) / 4));
   float* out = S > 1 ? partial : logits;

@@ -60,10 +60,11 @@ ROUTER_SHAPES = [
     (16, 256, 8),        # largest one-tile token count [1]
     (17, 256, 8),        # 64-row token tiles, 17 valid rows [2]
     (33, 512, 200),      # ragged tokens and experts [4]
-    (300, 512, 16),      # [4]
+    (300, 512, 16),      # LDS-tiled GEMM from T = 128 on [2]
+    (777, 1536, 200),    # tiled, ragged tokens and experts [6]
     (64, 7168, 256),     # decode batch [56]
     (16, 7168, 256),     # decode, wide [16]
-    (1000, 1024, 96),    # [8]
+    (1000, 1024, 96),    # [4]
     (4096, 256, 1024),   # enough output tiles: no K split [1]
 ]
 
