@@ -63,6 +63,7 @@ def _load():
                                                 p, p, p, p, p, p, p, i64, p]
         lib.orc_swiglu_requant.argtypes = [p, p, i32, p, p, p]
         lib.orc_expert_down.argtypes = [p, p, i32, i32, p, p, p]
+        lib.orc_dense_fp8.argtypes = [p, p, p, p, i32, i32, p, i64, p]
         lib.orc_layer_tokens.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p, p, p,
                                          p, i64, p, p, p, p]
         _lib = lib
@@ -263,4 +264,21 @@ def layer_tokens_shared(inp, logits, shared, tokens=None):
         _p(_c(inp.x, np.uint16)), _p(_c(logits, np.float32)), H, I, E, k,
         _p(inp.w1), _p(inp.s1), _p(inp.w3), _p(inp.s3), _p(inp.w2), _p(inp.s2), Is,
         *[(None if a is None else _p(a)) for a in sp], _p(toks), toks.size, _p(y))
+    return y
+
+
+# ------------------------------------------------------ FP8 dense projection
+def dense_fp8(xq, xs, wq, ws, tokens=None):
+    """y [ntok, N] fp64 = MXFP8 rows of x (xq [T, K], xs [T, K/32]) times the
+    FP8 weights (wq [N, K] e4m3, ws [N, K/32] E8M0), rows ``tokens``."""
+    xq = _c(xq, np.uint8)
+    xs = _c(xs, np.uint8)
+    wq = _c(wq, np.uint8)
+    ws = _c(ws, np.uint8)
+    T, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and xs.shape == (T, K // 32) and ws.shape == (N, K // 32)
+    toks = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
+    y = np.empty((toks.size, N), dtype=np.float64)
+    _load().orc_dense_fp8(_p(xq), _p(xs), _p(wq), _p(ws), N, K, _p(toks), toks.size, _p(y))
     return y

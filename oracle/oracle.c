@@ -26,6 +26,10 @@
  * output h) takes that decision on h rounded to fp32, the precision the GPU
  * kernels hold h in.  Routing compares the fp32 logits themselves.
  *
+ * Beside the layer: the router logits and the shared expert around it, and
+ * the FP8 dense projection (FP8 weights with per-32 E8M0 scales times MXFP8
+ * activations), each at the end of this file.
+ *
  * No blocking, no reordering: each function is the definition written out.
  */
 #include <math.h>
@@ -373,4 +377,38 @@ void orc_layer_tokens_shared(const uint16_t* x, const float* logits, int H, int 
   }
   free(ids); free(gates); free(xq); free(xs); free(G); free(U);
   free(h); free(hq); free(hs); free(O); free(acc);
+}
+
+/* ------------------------------------------------- FP8 dense projection */
+
+/* A dense (non-expert) linear layer with FP8 weights, the pages' second
+ * quantised workload ("FP8 dense projections": abstract of the arxivdaily
+ * page; the pwwt.cn review, section 5.3, names block-wise quantisation as the
+ * way FP8 pays off).  Weights W [N, K] are OCP e4m3 codes with one E8M0 scale per 32
+ * consecutive K elements of a row, activations the MXFP8 rows xq/xs of the
+ * path's own quantiser; y[t, n] = sum_k x[t, k] * W[n, k] over the decoded
+ * values, summed in fp64 in index order (each product of two scaled e4m3
+ * values is exact in fp64).  tokens lists the rows of x to compute; y is
+ * [ntok, N]. */
+void orc_dense_fp8(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                   int N, int K, const int32_t* tokens, long ntok, double* y) {
+  double* xd = (double*)malloc(sizeof(double) * (size_t)ntok * (size_t)K);
+  for (long i = 0; i < ntok; ++i) {
+    const long t = tokens[i];
+    for (int k = 0; k < K; ++k)
+      xd[i * K + k] = orc_e4m3(xq[t * K + k]) * orc_e8m0(xs[t * (K / 32) + k / 32]);
+  }
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    double* wd = (double*)malloc(sizeof(double) * (size_t)K);
+    for (int k = 0; k < K; ++k)
+      wd[k] = orc_e4m3(wq[(long)n * K + k]) * orc_e8m0(ws[(long)n * (K / 32) + k / 32]);
+    for (long i = 0; i < ntok; ++i) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) acc += xd[i * K + k] * wd[k];
+      y[i * N + n] = acc;
+    }
+    free(wd);
+  }
+  free(xd);
 }

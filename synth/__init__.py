@@ -32,6 +32,8 @@ TID_X, TID_LOGITS, TID_ZIPF, TID_W1, TID_S1, TID_W3, TID_S3, TID_W2, TID_S2 = ra
 # the router weights and the shared expert's weights (one more expert in the
 # same format as the routed ones)
 TID_WG, TID_SW1, TID_SS1, TID_SW3, TID_SS3, TID_SW2, TID_SS2 = range(9, 16)
+# the FP8 dense projection: activations, weight codes, weight scales
+TID_DX, TID_DW, TID_DS = range(16, 19)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -221,3 +223,46 @@ def make_shared_weights(sh: Shape, I_shared: int | None = None):
     w2 = random_bytes(sh.seed, TID_SW2, (1, H, Is // 2))
     s2 = uniform_codes(sh.seed, TID_SS2, (1, H, Is // 32), 121, 125)
     return w1, s1, w3, s3, w2, s2
+
+
+# ------------------------------------------------------ FP8 dense projection
+@dataclasses.dataclass(frozen=True)
+class DenseShape:
+    T: int
+    K: int
+    N: int
+    seed: int = 0
+
+
+DENSE_CONFIGS = {
+    "d0": DenseShape(T=5, K=256, N=96, seed=20),
+    "d1": DenseShape(T=8, K=16384, N=7168, seed=21),
+    "d3": DenseShape(T=4604, K=16384, N=7168, seed=23),
+}
+
+DENSE_NAMES = {
+    "d0": "dense tiny T5 K256 N96",
+    "d1": "dense-decode T8 K16384 N7168",
+    "d3": "dense-prefill T4604 K16384 N7168",
+}
+
+
+@dataclasses.dataclass
+class DenseInputs:
+    shape: DenseShape
+    x: np.ndarray    # [T, K] bf16 bits
+    wq: np.ndarray   # [N, K] e4m3 codes (no NaN codes)
+    ws: np.ndarray   # [N, K/32] E8M0 codes
+
+
+def make_dense_inputs(cfg, **overrides) -> DenseInputs:
+    """x bf16 N(0, 1); weight codes uniform over the 254 non-NaN e4m3 bytes;
+    weight scale codes uniform over {118..122} (2^-9 .. 2^-5)."""
+    sh = DENSE_CONFIGS[cfg] if isinstance(cfg, str) else cfg
+    if overrides:
+        sh = dataclasses.replace(sh, **overrides)
+    x = f32_to_bf16_bits(normal_f32(sh.seed, TID_DX, (sh.T, sh.K), 1.0))
+    c = uniform_codes(sh.seed, TID_DW, (sh.N, sh.K), 0, 253)
+    wq = (c + (c >= 0x7F)).astype(np.uint8)          # skip 0x7F; 253 + 1 = 0xFE tops out below 0xFF
+    ws = uniform_codes(sh.seed, TID_DS, (sh.N, sh.K // 32), 118, 122)
+    return DenseInputs(shape=sh, x=x, wq=wq, ws=ws)
