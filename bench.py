@@ -21,6 +21,9 @@ logits come from a bf16 GEMM and --n-shared shared experts, packed after the
 routed ones, join every token's slots; the router's HIP-event time (the
 stand-alone call, GEMM plus slice sum) and its roofline against HBM are
 reported beside the gate/up kernel's.
+
+--config d1 / d3 measures the FP8 dense projection instead (one step = MXFP8
+quantisation of x + moe_fp8_dense_forward), with its own roofline line.
 """
 from __future__ import annotations
 
@@ -207,12 +210,102 @@ def cpu_baseline(name: str, budget_s: float):
                       f"{n_tok // T}x in {dt:.1f} s (fp64 plain C, OpenMP)"}
 
 
+def cpu_baseline_dense(name: str, budget_s: float):
+    import oracle
+    import synth
+    inp = synth.make_dense_inputs(name)
+    xq, xs = oracle.quant_mxfp8_bf16(inp.x)
+    n_tok = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.dense_fp8(xq, xs, inp.wq, inp.ws, np.array([n_tok % inp.shape.T], dtype=np.int32))
+        n_tok += 1
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tok} single-token rows of the {name} projection in {dt:.1f} s "
+                      f"(fp64 plain C, OpenMP over the output rows; x quantised beforehand)"}
+
+
+def bench_dense(args):
+    """One step = moe_quant_act_mxfp8 + moe_fp8_dense_forward on one batch of rows."""
+    import torch
+
+    import fp4_routed_expert_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    inp = synth.make_dense_inputs(args.config)
+    sh = inp.shape
+    T, K, N = sh.T, sh.K, sh.N
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    wq, ws = t(inp.wq), t(inp.ws)
+    nbytes = moe._lib.lib().moe_fp8_dense_packed_bytes(N, K)
+    copies = args.copies or max(1, min(8, int(np.ceil(2.0e9 / nbytes))))
+    dws = [moe.dense_prepack(wq, ws) for _ in range(copies)]
+    del wq, ws
+    x = t(inp.x.view(np.int16)).view(torch.bfloat16)
+    xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, K // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i, timed=None):
+        moe.quant_act_mxfp8(x, xq, xs)
+        if timed is not None:
+            ev[timed][0].record()
+        moe.dense_forward(dws[i % copies], xq, xs, args.flags, y=y)
+        if timed is not None:
+            ev[timed][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    decode = args.flags == 1 or (args.flags == 0 and T <= 32)
+    b_alg = N * K * (1 + 1 / 32) + T * K * (1 + 1 / 32) + T * N * 2
+    f_alg = 2.0 * T * N * K
+    if decode:
+        ach = b_alg / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "dense_decode_kernel (FP8 weight streaming)", "achieved": ach,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                "alg_bytes_per_launch": b_alg, "avg_launch_us": k_ms * 1e3}
+    else:
+        ach = f_alg / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "dense_prefill_kernel (LDS-tiled FP8 GEMM)", "achieved": ach,
+                "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_FP8_PEAK_TFLOPS,
+                "traffic": None, "alg_flops_per_launch": f_alg, "avg_launch_us": k_ms * 1e3}
+    ms = dt / args.steps * 1e3
+    line = {
+        "metric": "FP8 dense projection tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU",
+        "value": T * args.steps / dt, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3xfp8e4m3->bf16", "data": "synthetic",
+        "config": {"workload": synth.DENSE_NAMES.get(args.config, args.config), "T": T, "K": K, "N": N,
+                   "seed": sh.seed, "weight_copies": copies, "path_flags": args.flags, "launch": "eager"},
+        "roofline": roof,
+        "cpu_baseline": cpu_baseline_dense(args.config, args.cpu_budget) if args.cpu_budget > 0 else None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c1", help="workload name (c1 is the measured one)")
+    ap.add_argument("--config", default="c1",
+                    help="workload name: c0-c4 the MoE layer (c1 is the measured one), d0-d3 the FP8 "
+                         "dense projection")
     ap.add_argument("--flags", type=int, default=0, help="1 = force decode path, 2 = force prefill path")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 = skip")
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0 = auto)")
@@ -237,6 +330,12 @@ def main():
     if args.traffic_summary:
         print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.kernel, args.workload,
                               args.config, args.steps))
+        return
+    if args.config.startswith("d"):
+        if args.gpus != 1:
+            print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+            sys.exit(2)
+        bench_dense(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

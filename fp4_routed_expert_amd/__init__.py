@@ -25,7 +25,8 @@ __all__ = [
     "forward_workspace_size", "layer_forward", "layer_workspace_size", "router_logits",
     "router_workspace_size",
     "shared_workspace_size", "shared_expert", "combine_shared", "layer_full_workspace_size",
-    "layer_forward_full", "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
+    "layer_forward_full", "DenseWeights", "dense_prepack", "dense_forward", "dense_layer",
+    "MOE_FLAG_FORCE_DECODE", "MOE_FLAG_FORCE_PREFILL", "MoeError",
 ]
 
 
@@ -329,3 +330,52 @@ def layer_forward_full(pw: PackedWeights, n_shared: int, router_w: torch.Tensor,
         ctypes.byref(pw.desc), n_shared, _ptr(router_w), _ptr(x), T, k, _ptr(y), _ptr(workspace),
         workspace.numel(), flags, _stream(x)), "moe_fp4_layer_forward_full")
     return y
+
+
+# ------------------------------------------------------ FP8 dense projection
+@dataclasses.dataclass
+class DenseWeights:
+    """Prepacked FP8 dense weights: the device buffer plus the plain-C descriptor."""
+    buffer: torch.Tensor
+    desc: _lib.MoeFp8DenseWeights
+
+    @property
+    def N(self):
+        return self.desc.N
+
+    @property
+    def K(self):
+        return self.desc.K
+
+
+def dense_prepack(wq, ws) -> DenseWeights:
+    """wq [N, K] e4m3 codes, ws [N, K/32] E8M0 codes (uint8 device tensors)."""
+    _check_dtype(wq, (torch.uint8,), "wq")
+    _check_dtype(ws, (torch.uint8,), "ws")
+    N, K = wq.shape
+    nbytes = int(_lib.lib().moe_fp8_dense_packed_bytes(N, K))
+    if nbytes == 0:
+        raise MoeError(_lib.MOE_ERR_UNSUPPORTED, "moe_fp8_dense_packed_bytes")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=wq.device)
+    desc = _lib.MoeFp8DenseWeights()
+    _lib.check(_lib.lib().moe_fp8_dense_prepack(_ptr(wq), _ptr(ws), N, K, _ptr(buf), nbytes,
+                                                ctypes.byref(desc), _stream(wq)),
+               "moe_fp8_dense_prepack")
+    return DenseWeights(buffer=buf, desc=desc)
+
+
+def dense_forward(dw: DenseWeights, xq, xs, flags: int = 0, y=None):
+    """y [T, N] bf16 = MXFP8 rows (xq [T, K], xs [T, K/32]) times the FP8 dense weights."""
+    T = xq.shape[0]
+    if y is None:
+        y = torch.empty((T, dw.N), dtype=torch.bfloat16, device=xq.device)
+    _check_dtype(y, (torch.bfloat16,), "y")
+    _lib.check(_lib.lib().moe_fp8_dense_forward(ctypes.byref(dw.desc), _ptr(xq), _ptr(xs), T, _ptr(y),
+                                                flags, _stream(xq)), "moe_fp8_dense_forward")
+    return y
+
+
+def dense_layer(dw: DenseWeights, x: torch.Tensor, flags: int = 0):
+    """bf16 x [T, K] -> MXFP8 (moe_quant_act_mxfp8) -> y [T, N] bf16."""
+    xq, xs = quant_act_mxfp8(x)
+    return dense_forward(dw, xq, xs, flags)

@@ -21,6 +21,7 @@ MOE_ERR_HIP = 4
 MOE_FLAG_FORCE_DECODE = 1
 MOE_FLAG_FORCE_PREFILL = 2
 MOE_FP4_LAYOUT_VERSION = 1
+MOE_FP8_DENSE_LAYOUT_VERSION = 1
 
 
 class MoeFp4Weights(ctypes.Structure):
@@ -28,6 +29,16 @@ class MoeFp4Weights(ctypes.Structure):
         ("E", ctypes.c_int32),
         ("H", ctypes.c_int32),
         ("I", ctypes.c_int32),
+        ("layout_version", ctypes.c_uint32),
+        ("packed", ctypes.c_void_p),
+        ("packed_bytes", ctypes.c_size_t),
+    ]
+
+
+class MoeFp8DenseWeights(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32),
+        ("K", ctypes.c_int32),
         ("layout_version", ctypes.c_uint32),
         ("packed", ctypes.c_void_p),
         ("packed_bytes", ctypes.c_size_t),
@@ -47,6 +58,7 @@ _I32 = ctypes.c_int32
 _U32 = ctypes.c_uint32
 _SZ = ctypes.c_size_t
 _WP = ctypes.POINTER(MoeFp4Weights)
+_DP = ctypes.POINTER(MoeFp8DenseWeights)
 
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -75,6 +87,9 @@ SIGNATURES = {
     "moe_fp4_layer_full_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _U32]),
     "moe_fp4_layer_forward_full": (ctypes.c_int, [_WP, _I32, _P, _P, _I32, _I32, _P, _P, _SZ, _U32,
                                                   _P]),
+    "moe_fp8_dense_packed_bytes": (_SZ, [_I32, _I32]),
+    "moe_fp8_dense_prepack": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _SZ, _DP, _P]),
+    "moe_fp8_dense_forward": (ctypes.c_int, [_DP, _P, _P, _I32, _P, _U32, _P]),
 }
 
 

@@ -175,6 +175,24 @@ struct PackedLayout {
   }
 };
 
+// ------------------------------------------------- FP8 dense weight layout
+// Tile (nt, j): weight rows 16 nt .. +16, K 128 j .. +128, 2 KiB in the e4m3
+// MFMA operand's lane order (lane l = 16 g + r: row r, K [16 g, +16) in the
+// first KiB, K [64 + 16 g, +16) in the second); tiles of one row group are
+// consecutive along K.  Scales: 64 bytes per tile, byte l = row r, block g.
+struct DenseLayout {
+  int N, K, J;
+  size_t s_off, total;
+  __host__ __device__ DenseLayout(int N_, int K_) : N(N_), K(K_), J(K_ / 128) {
+    s_off = PackedLayout::align256((size_t)(N / 16) * J * 2048);
+    total = PackedLayout::align256(s_off + (size_t)(N / 16) * J * 64);
+  }
+  __host__ __device__ size_t tile_off(int nt, int j) const { return ((size_t)nt * J + j) * 2048; }
+  __host__ __device__ size_t scale_off(int nt, int j) const {
+    return s_off + ((size_t)nt * J + j) * 64;
+  }
+};
+
 // ------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch(es).
 constexpr int kFrontMaxT = 32;  // token counts taken by the fused front kernel
@@ -225,5 +243,11 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wg, int T, int H, in
 hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
                                   float* logits, float* partial, hipStream_t s);
 hipError_t launch_identity_route(int T, int32_t* sorted_pair, int32_t* offsets, hipStream_t s);
+hipError_t launch_dense_pack(const uint8_t* wq, const uint8_t* ws, int N, int K, uint8_t* packed,
+                             hipStream_t s);
+hipError_t launch_dense_decode(const uint8_t* packed, const uint8_t* xq, const uint8_t* xs, int T,
+                               int N, int K, uint16_t* y, hipStream_t s);
+hipError_t launch_dense_prefill(const uint8_t* packed, const uint8_t* xq, const uint8_t* xs, int T,
+                                int N, int K, uint16_t* y, hipStream_t s);
 
 }  // namespace moe

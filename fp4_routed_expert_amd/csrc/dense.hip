@@ -1,0 +1,313 @@
+// FP8 dense projection: y[t, n] = sum_k x[t, k] * W[n, k] with W in OCP e4m3
+// and one E8M0 scale per 32 consecutive K elements of a row, x as the MXFP8
+// rows of the path's activation quantiser, fp32 accumulation in the gfx950
+// scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, both operands e4m3, the
+// block scales applied in hardware) and y stored as bf16 (RNE).  The pages
+// list "FP8 dense projections" beside the FP4 routed experts (abstract of the
+// arxivdaily page) and name block-wise quantisation as the way FP8 pays off
+// (pwwt.cn review, section 5.3); matrix-multiply outputs may be low precision
+// while the accumulation stays fp32 (same review, section 4.1).
+//
+// Packed weights: tile (nt, j) = rows 16 nt .. +16, K 128 j .. +128, 2 KiB in
+// the MFMA operand's lane order -- lane l = 16 g + r holds row r's K elements
+// [16 g, 16 g + 16) in the first KiB and [64 + 16 g, +16) in the second (the
+// e4m3 operand layout measured on gfx950), so a wave loads a tile with two
+// fully contiguous 1 KiB runs; its 64 scale bytes follow the same lanes (lane
+// l: row r, 32-block g).  Tiles of one row group are consecutive along K.
+//
+// Decode (few tokens): weight streaming.  A workgroup owns one 16-row group
+// and one 16-token tile; its waves split K and each keeps a batch of tiles in
+// flight; partial sums meet in LDS in wave order.  Prefill: LDS-tiled GEMM,
+// 128 tokens x 128 rows per workgroup, 128 K per stage, two register sets so
+// that one stage loads while another multiplies.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8i cat8(v4u lo, v4u hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ v4f mfma_fp8_fp8(v8i a, v8i b, v4f c, int sa, int sb) {
+  // cbsz = 0, blgp = 0: both operands e4m3; scale bytes from byte 0 of sa / sb
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// ----------------------------------------------------------------- prepack
+// One thread per (tile, lane): canonical wq [N, K], ws [N, K/32] -> packed.
+__global__ __launch_bounds__(256) void dense_pack_kernel(const uint8_t* __restrict__ wq,
+                                                         const uint8_t* __restrict__ ws, int N,
+                                                         int K, uint8_t* __restrict__ packed) {
+  const DenseLayout L(N, K);
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long ntiles = (long)(N / 16) * L.J;
+  if (i >= ntiles * 64) return;
+  const long tile = i >> 6;
+  const int lane = (int)(i & 63), r = lane & 15, g = lane >> 4;
+  const int nt = (int)(tile / L.J), j = (int)(tile % L.J);
+  const long row = 16L * nt + r;
+  const uint8_t* src = wq + row * K + 128L * j;
+  uint8_t* dst = packed + L.tile_off(nt, j);
+  *reinterpret_cast<uint4*>(dst + lane * 16) = *reinterpret_cast<const uint4*>(src + 16 * g);
+  *reinterpret_cast<uint4*>(dst + 1024 + lane * 16) = *reinterpret_cast<const uint4*>(src + 64 + 16 * g);
+  packed[L.scale_off(nt, j) + lane] = ws[row * (K / 32) + 4L * j + g];
+}
+
+// ------------------------------------------------------------------ decode
+// One K-step of a wave: the weight tile, its scale byte, the activation
+// fragment (token row r, the same two 16-byte pieces) and its scale byte.
+struct DStep {
+  v4u b0, b1, a0, a1;
+  uint32_t sb, sa;
+};
+
+__device__ __forceinline__ void dload(DStep& s, const uint8_t* wt, const uint8_t* st,
+                                      const uint8_t* arow, const uint8_t* as, int j) {
+  const uint8_t* w = wt + (size_t)j * 2048;
+  s.b0 = *reinterpret_cast<const v4u*>(w);
+  s.b1 = *reinterpret_cast<const v4u*>(w + 1024);
+  s.sb = st[(size_t)j * 64];
+  s.a0 = *reinterpret_cast<const v4u*>(arow + (size_t)j * 128);
+  s.a1 = *reinterpret_cast<const v4u*>(arow + (size_t)j * 128 + 64);
+  s.sa = as[(size_t)j * 4];
+}
+
+template <int NW, int kB>
+__global__ __launch_bounds__(64 * NW) void dense_decode_kernel(const uint8_t* __restrict__ packed,
+                                                               const uint8_t* __restrict__ xq,
+                                                               const uint8_t* __restrict__ xs,
+                                                               int T, int N, int K,
+                                                               uint16_t* __restrict__ y) {
+  const DenseLayout L(N, K);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nt = blockIdx.x, mt = blockIdx.y;
+  const int J = L.J;
+  const int j0 = (wave * J) / NW, j1 = ((wave + 1) * J) / NW;
+  // this lane's pieces: weight tile lane offset, activation row 16 mt + r
+  // (clamped: rows past T are computed from the last row and never stored)
+  const uint8_t* wt = packed + L.tile_off(nt, 0) + lane * 16;
+  const uint8_t* st = packed + L.scale_off(nt, 0) + lane;
+  const int trow = min(16 * mt + r, T - 1);
+  const uint8_t* arow = xq + (size_t)trow * K + 16 * g;
+  const uint8_t* as = xs + (size_t)trow * (K / 32) + g;
+
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  DStep s[kB];
+  int j = j0;
+  // whole batches: kB steps' loads back to back, then their MFMAs
+  for (; j + kB <= j1; j += kB) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u) dload(s[u], wt, st, arow, as, j + u);
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      acc = mfma_fp8_fp8(cat8(s[u].a0, s[u].a1), cat8(s[u].b0, s[u].b1), acc, (int)s[u].sa,
+                         (int)s[u].sb);
+  }
+  for (; j < j1; ++j) {
+    dload(s[0], wt, st, arow, as, j);
+    acc = mfma_fp8_fp8(cat8(s[0].a0, s[0].a1), cat8(s[0].b0, s[0].b1), acc, (int)s[0].sa,
+                       (int)s[0].sb);
+  }
+
+  // fixed-order sum of the waves' partials, then bf16 stores of the valid tokens
+  __shared__ v4f red[NW][64];
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  v4f a = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) a += red[w][lane];
+  const int n = 16 * nt + r;  // D column = weight row
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t = 16 * mt + 4 * g + v;  // D row = token
+    if (t < T) y[(size_t)t * N + n] = f32_to_bf16(a[v]);
+  }
+}
+
+// ----------------------------------------------------------------- prefill
+constexpr int kDB = 128;                        // tokens and weight rows per tile
+constexpr int kDA = kDB * 128;                  // A bytes per stage (128 rows x 128 K)
+constexpr int kDBw = 8 * 2048;                  // B bytes per stage (8 packed tiles)
+constexpr int kDStage = kDA + kDBw + 512 + 512;  // + A scales (dword per row) + B scales
+
+struct DLoad {
+  v4u a[4], b[4];
+  uint32_t sc;  // threads < 128: x row tid's scale dword; others: a weight tile's scale dword
+};
+
+__device__ __forceinline__ int dswz(int row, int q) { return row * 128 + ((q ^ (row & 7)) << 4); }
+
+// Global sources of one thread for the stage at K-step j: 4 x rows (32 apart)
+// at granule lq, 4 16-byte chunks of the weight tiles btile + 2 i, and (threads
+// below 128) the scale dwords of x row tid and of weight tile tid >> 4.
+struct DSrc {
+  uint32_t a[4], b[4];     // byte offsets from xq and packed (all < 2^32)
+  const uint8_t* sbase;    // xs (threads < 128) or packed
+  uint32_t soff, sstep;    // scale dword offset at K-step 0, bytes per K-step
+};
+
+// Loads K-step min(j, J - 1); a step j >= J (the padding step of an odd
+// count) is zeroed instead, so its products are exact zeros.
+__device__ __forceinline__ void dense_gload(DLoad& d, const uint8_t* __restrict__ xq,
+                                            const uint8_t* __restrict__ packed, const DSrc& g,
+                                            int j, int J) {
+  const uint32_t live = j < J ? ~0u : 0u;  // uniform: a mask, not a branch
+  const uint32_t jj = (uint32_t)min(j, J - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d.a[i] = *reinterpret_cast<const v4u*>(xq + (g.a[i] + 128u * jj)) & live;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d.b[i] = *reinterpret_cast<const v4u*>(packed + (g.b[i] + 2048u * jj)) & live;
+  d.sc = *reinterpret_cast<const uint32_t*>(g.sbase + (g.soff + g.sstep * jj));
+}
+
+// LDS stage: A rows (swizzled) | 8 weight tiles | 128 A scale dwords | 128 B
+// scale dwords (thread tid writes dword tid of the last two).
+__device__ __forceinline__ void dense_lstore(const DLoad& d, uint8_t* buf, int lr, int lq,
+                                             int boff, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(buf + dswz(32 * i + lr, lq)) = d.a[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(buf + kDA + boff + 4096 * i) = d.b[i];
+  *reinterpret_cast<uint32_t*>(buf + kDA + kDBw + 4 * tid) = d.sc;
+}
+
+// One stage's 16 MFMAs of a wave (4 token sub-tiles x 4 weight tiles).
+__device__ __forceinline__ void dense_compute(v4f (&acc)[4][4], const uint8_t* cur, int wm, int wn,
+                                              int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  v8i b[4];
+  int sb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint8_t* tb = cur + kDA + (4 * wn + t) * 2048 + 16 * lane;
+    b[t] = cat8(*reinterpret_cast<const v4u*>(tb), *reinterpret_cast<const v4u*>(tb + 1024));
+    sb[t] = cur[kDA + kDBw + 512 + (4 * wn + t) * 64 + lane];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 64 * wm + 16 * i + r;
+    const v8i a = cat8(*reinterpret_cast<const v4u*>(cur + dswz(row, g)),
+                       *reinterpret_cast<const v4u*>(cur + dswz(row, 4 + g)));
+    const int sa = cur[kDA + kDBw + 4 * row + g];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = mfma_fp8_fp8(a, b[t], acc[i][t], sa, sb[t]);
+  }
+}
+
+__global__ __launch_bounds__(256) void dense_prefill_kernel(const uint8_t* __restrict__ packed,
+                                                            const uint8_t* __restrict__ xq,
+                                                            const uint8_t* __restrict__ xs, int T,
+                                                            int N, int K,
+                                                            uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kDStage];
+  const DenseLayout L(N, K);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int NTn = (N + kDB - 1) / kDB;
+  // weight-row tiles vary fastest: the token tile's x rows stay in L2 while its
+  // row tiles go by, consecutive workgroups of an XCD (block % 8) share them
+  const int bn = (int)(blockIdx.x % (unsigned)NTn), bm = (int)(blockIdx.x / (unsigned)NTn);
+  const int m0 = bm * kDB, nt0 = bn * 8;  // first 16-row weight tile
+  const int ntiles = N / 16;
+  const int J = L.J;
+
+  // global sources of this thread: 4 x rows (32 apart), granule lq; 4 chunks of
+  // the 8 weight tiles (tile (tid >> 7) + 2 i, 16 bytes (tid & 127)); the scale
+  // dwords of x row tid and of weight tile tid >> 4 (threads < 128)
+  const int lr = tid >> 3, lq = tid & 7;
+  const int btile = tid >> 7;  // chunk i covers weight tile btile + 2 i
+  const int boff = btile * 2048 + 16 * (tid & 127);
+  DSrc src;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) src.a[i] = (uint32_t)min(m0 + 32 * i + lr, T - 1) * (uint32_t)K + 16 * lq;
+  // weight tiles past N are clamped to the last one (their columns are never
+  // stored), so each chunk keeps its own base
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    src.b[i] = (uint32_t)L.tile_off(min(nt0 + btile + 2 * i, ntiles - 1), 0) + 16 * (tid & 127);
+  if (tid < 128) {
+    src.sbase = xs;
+    src.soff = (uint32_t)min(m0 + tid, T - 1) * (uint32_t)(K / 32);
+    src.sstep = 4;
+  } else {
+    src.sbase = packed;
+    src.soff = (uint32_t)L.scale_off(min(nt0 + ((tid - 128) >> 4), ntiles - 1), 0) + 4 * (tid & 15);
+    src.sstep = 64;
+  }
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Stage j + 2 loads while j multiplies and j + 1 goes to the idle buffer.
+  // The steps run in pairs; an odd count gets a zero padding step (a step
+  // left over after the loop would make the compiler rename the
+  // accumulators, doubling their registers).
+  const int J2 = J + (J & 1);
+  DLoad p, q;
+  dense_gload(p, xq, packed, src, 0, J);
+  dense_gload(q, xq, packed, src, 1, J);
+  dense_lstore(p, lds, lr, lq, boff, tid);
+  __syncthreads();
+  uint8_t* const buf0 = lds;
+  uint8_t* const buf1 = lds + kDStage;
+  for (int j = 0; j < J2; j += 2) {
+    dense_gload(p, xq, packed, src, j + 2, J);
+    dense_compute(acc, buf0, wm, wn, lane);
+    dense_lstore(q, buf1, lr, lq, boff, tid);
+    __syncthreads();
+    dense_gload(q, xq, packed, src, j + 3, J);
+    dense_compute(acc, buf1, wm, wn, lane);
+    dense_lstore(p, buf0, lr, lq, boff, tid);
+    __syncthreads();
+  }
+
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = 16 * (nt0 + 4 * wn + t) + r;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = m0 + 64 * wm + 16 * i + 4 * g + v;
+        if (tok < T) y[(size_t)tok * N + n] = f32_to_bf16(acc[i][t][v]);
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dense_pack(const uint8_t* wq, const uint8_t* ws, int N, int K, uint8_t* packed,
+                             hipStream_t s) {
+  const long threads = (long)(N / 16) * (K / 128) * 64;
+  hipLaunchKernelGGL(dense_pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     wq, ws, N, K, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_decode(const uint8_t* packed, const uint8_t* xq, const uint8_t* xs, int T,
+                               int N, int K, uint16_t* y, hipStream_t s) {
+  const dim3 grid((unsigned)(N / 16), (unsigned)((T + 15) / 16));
+  hipLaunchKernelGGL((dense_decode_kernel<8, 4>), grid, dim3(512), 0, s, packed, xq, xs, T, N, K, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_prefill(const uint8_t* packed, const uint8_t* xq, const uint8_t* xs, int T,
+                                int N, int K, uint16_t* y, hipStream_t s) {
+  const long blocks = (long)((T + kDB - 1) / kDB) * ((N + kDB - 1) / kDB);
+  hipLaunchKernelGGL(dense_prefill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, xq, xs,
+                     T, N, K, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

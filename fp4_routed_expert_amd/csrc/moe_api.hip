@@ -22,6 +22,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
+constexpr int kDenseDecodeMaxT = 32;  // dense projection: weight streaming up to 2 token tiles
 
 // Common checks of (T, E, k): negative or zero sizes are invalid, shapes
 // outside the kernels' coverage unsupported.
@@ -522,6 +523,65 @@ moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w, int32_t n_sh
                                  reinterpret_cast<const int32_t*>(lw + lc.sorted),
                                  reinterpret_cast<const int32_t*>(lw + lc.pos), T, kk, y,
                                  lw + lc.fwd, lc.fwd_bytes, flags, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- FP8 dense projection
+extern "C" {
+
+static moe_status_t check_dense_nk(int32_t N, int32_t K) {
+  if (N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (N % 16 != 0 || K % 128 != 0 || N > (1 << 20) || K > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  if (DenseLayout(N, K).total >= ((size_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_fp8_dense_packed_bytes(int32_t N, int32_t K) {
+  if (check_dense_nk(N, K) != MOE_OK) return 0;
+  return DenseLayout(N, K).total;
+}
+
+moe_status_t moe_fp8_dense_prepack(const uint8_t* wq, const uint8_t* ws, int32_t N, int32_t K,
+                                   void* packed, size_t packed_bytes, moe_fp8_dense_weights_t* desc,
+                                   hipStream_t stream) {
+  moe_status_t st = check_dense_nk(N, K);
+  if (st != MOE_OK) return st;
+  if (!wq || !ws || !packed || !desc) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(wq, 16) || !aligned(packed, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  const DenseLayout L(N, K);
+  if (packed_bytes < L.total) return MOE_ERR_INVALID_ARGUMENT;
+  st = hip_status(launch_dense_pack(wq, ws, N, K, static_cast<uint8_t*>(packed), stream));
+  if (st != MOE_OK) return st;
+  desc->N = N;
+  desc->K = K;
+  desc->layout_version = MOE_FP8_DENSE_LAYOUT_VERSION;
+  desc->packed = packed;
+  desc->packed_bytes = packed_bytes;
+  return MOE_OK;
+}
+
+moe_status_t moe_fp8_dense_forward(const moe_fp8_dense_weights_t* w, const uint8_t* xq,
+                                   const uint8_t* xs, int32_t T, uint16_t* y, uint32_t flags,
+                                   hipStream_t stream) {
+  if (!w) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->layout_version != MOE_FP8_DENSE_LAYOUT_VERSION || !w->packed) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_dense_nk(w->N, w->K);
+  if (st != MOE_OK) return st;
+  if (w->packed_bytes < DenseLayout(w->N, w->K).total || !aligned(w->packed, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (T < 0) return MOE_ERR_INVALID_ARGUMENT;
+  const bool fd = flags & MOE_FLAG_FORCE_DECODE, fp = flags & MOE_FLAG_FORCE_PREFILL;
+  if ((flags & ~(MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_PREFILL)) != 0 || (fd && fp))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)T * w->K >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!xq || !xs || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(xq, 16) || !aligned(xs, 4) || !aligned(y, 2)) return MOE_ERR_INVALID_ARGUMENT;
+  const uint8_t* pk = static_cast<const uint8_t*>(w->packed);
+  const bool decode = fd || (!fp && T <= kDenseDecodeMaxT);
+  if (decode) return hip_status(launch_dense_decode(pk, xq, xs, T, w->N, w->K, y, stream));
+  return hip_status(launch_dense_prefill(pk, xq, xs, T, w->N, w->K, y, stream));
 }
 
 }  // extern "C"

@@ -309,6 +309,44 @@ moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/, i
                                         size_t workspace_bytes, uint32_t flags,
                                         hipStream_t stream);
 
+/*
+ * FP8 dense projection (a non-expert linear layer): y[t, n] = sum_k x[t, k] *
+ * W[n, k].  W is OCP e4m3 with one E8M0 scale per 32 consecutive K elements
+ * of a row (block-wise FP8: the pages list "FP8 dense projections" beside the
+ * FP4 experts, arxivdaily abstract, and name block-wise quantisation as the
+ * way FP8 pays off, pwwt.cn review, section 5.3); x is given as MXFP8 rows
+ * (moe_quant_act_mxfp8); the products accumulate in fp32 in the scaled MFMA
+ * and y is stored as bf16, RNE (pwwt.cn review, section 4.1: low-precision
+ * matrix-multiply outputs, fp32 accumulation).
+ *
+ * moe_fp8_dense_prepack: wq [N, K] e4m3 codes (16-byte aligned), ws [N, K/32]
+ * E8M0 -> `packed` (device, >= moe_fp8_dense_packed_bytes(N, K) bytes,
+ * 256-byte aligned) in the kernels' tile order, and `desc` (host), as for the
+ * expert weights.  N % 16 == 0, K % 128 == 0, packed size < 4 GiB.
+ *
+ * moe_fp8_dense_forward: xq [T, K] (16-byte aligned), xs [T, K/32] (4-byte
+ * aligned), y [T, N] bf16 bits (out).  T * K < 2^32.  Path: weight streaming
+ * for T <= 32 (MOE_FLAG_FORCE_DECODE for any T), an LDS-tiled GEMM otherwise
+ * (MOE_FLAG_FORCE_PREFILL for any T); both compute the same function.  No
+ * workspace; the same inputs give the same bits.
+ */
+#define MOE_FP8_DENSE_LAYOUT_VERSION 1u
+
+typedef struct moe_fp8_dense_weights {
+  int32_t N, K;
+  uint32_t layout_version;
+  const void* packed;   /* device */
+  size_t packed_bytes;
+} moe_fp8_dense_weights_t;
+
+size_t moe_fp8_dense_packed_bytes(int32_t N, int32_t K);
+moe_status_t moe_fp8_dense_prepack(const uint8_t* wq, const uint8_t* ws, int32_t N, int32_t K,
+                                   void* packed, size_t packed_bytes,
+                                   moe_fp8_dense_weights_t* desc /*(host)*/, hipStream_t stream);
+moe_status_t moe_fp8_dense_forward(const moe_fp8_dense_weights_t* w /*(host)*/,
+                                   const uint8_t* xq, const uint8_t* xs, int32_t T, uint16_t* y,
+                                   uint32_t flags, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

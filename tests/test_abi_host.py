@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 26, names
     so = ctypes.CDLL(_lib.SO_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -196,6 +196,37 @@ def test_router_and_shared_argument_errors():
     assert lf(ctypes.byref(d), 0, MIS, A, 16, 2, A, A, n0, 0, NUL) == INV
     assert lf(ctypes.byref(d), 0, A, A, 16, 2, A, A, n0, 3, NUL) == INV       # both paths forced
     assert lf(ctypes.byref(d), 0, NUL, NUL, 0, 2, NUL, NUL, 0, 0, NUL) == 0   # T = 0
+
+
+def test_dense_argument_errors():
+    nb = L.moe_fp8_dense_packed_bytes(7168, 16384)
+    assert 7168 * 16384 * (1 + 1 / 32) <= nb <= 7168 * 16384 * (1 + 1 / 32) + 512
+    assert L.moe_fp8_dense_packed_bytes(100, 256) == 0         # N % 16
+    assert L.moe_fp8_dense_packed_bytes(96, 200) == 0          # K % 128
+    d = _lib.MoeFp8DenseWeights()
+    pre = L.moe_fp8_dense_prepack
+    nb0 = L.moe_fp8_dense_packed_bytes(96, 256)
+    assert pre(A, A, 96, 200, A, nb0, ctypes.byref(d), NUL) == UNS
+    assert pre(A, A, 96, 256, A, nb0 - 1, ctypes.byref(d), NUL) == INV
+    assert pre(A, A, 96, 256, MIS, nb0, ctypes.byref(d), NUL) == INV
+    assert pre(MIS, A, 96, 256, A, nb0, ctypes.byref(d), NUL) == INV
+    assert pre(A, A, 0, 256, A, nb0, ctypes.byref(d), NUL) == INV
+    d.N, d.K, d.layout_version, d.packed, d.packed_bytes = 96, 256, 1, 1 << 20, nb0
+    fw = L.moe_fp8_dense_forward
+    assert fw(ctypes.byref(d), A, A, 0, NUL, 0, NUL) == 0            # T = 0
+    assert fw(ctypes.byref(d), A, A, -1, A, 0, NUL) == INV
+    assert fw(ctypes.byref(d), A, A, 4, A, 3, NUL) == INV            # both paths forced
+    assert fw(ctypes.byref(d), MIS, A, 4, A, 0, NUL) == INV          # xq not 16-aligned
+    assert fw(ctypes.byref(d), A, NUL, 4, A, 0, NUL) == INV
+    big = _lib.MoeFp8DenseWeights()
+    big.N, big.K, big.layout_version, big.packed = 96, 1 << 20, 1, 1 << 20
+    big.packed_bytes = L.moe_fp8_dense_packed_bytes(96, 1 << 20)
+    assert fw(ctypes.byref(big), A, A, 4096, A, 0, NUL) == UNS        # T * K >= 2^32
+    d.layout_version = 2
+    assert fw(ctypes.byref(d), A, A, 4, A, 0, NUL) == INV
+    d.layout_version = 1
+    d.packed_bytes = nb0 - 1
+    assert fw(ctypes.byref(d), A, A, 4, A, 0, NUL) == INV
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,124 @@
+"""GPU parity of the FP8 dense projection, through the C ABI.
+
+y (bf16) against the oracle's fp64 sums on the same MXFP8 rows, on both
+paths (weight streaming and the LDS-tiled GEMM): the tiny workload, ragged
+token counts, an odd K-step count (the tiled kernel's zero padding step),
+weight-row counts that leave a partial 128-row tile, the decode-shaped and
+prefill-shaped projections at full size (sampled tokens), plus the prepacked
+layout read back bit for bit and a one-hot weight whose outputs are exact."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_routed_expert_amd as moe
+import oracle
+import synth
+from gpu_cases import check_y, log, sample_tokens, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DEC, PRE = moe.MOE_FLAG_FORCE_DECODE, moe.MOE_FLAG_FORCE_PREFILL
+
+
+class DenseCase:
+    def __init__(self, cfg, dev, **over):
+        self.inp = synth.make_dense_inputs(cfg, **over)
+        self.sh = self.inp.shape
+        self.x = to_dev(self.inp.x.view(np.int16), dev).view(torch.bfloat16)
+        self.dw = moe.dense_prepack(to_dev(self.inp.wq, dev), to_dev(self.inp.ws, dev))
+        self.xq, self.xs = oracle.quant_mxfp8_bf16(self.inp.x)
+        torch.cuda.synchronize()
+
+    def ref(self, toks):
+        return oracle.dense_fp8(self.xq, self.xs, self.inp.wq, self.inp.ws, toks)
+
+
+_cache = {}
+
+
+def get_dense(key, dev, **over):
+    k = (key, tuple(sorted(over.items())))
+    if k not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        log(f"[dense case] {k}")
+        _cache[k] = DenseCase(key, dev, **over)
+    return _cache[k]
+
+
+SMALL = [
+    ("d0", {}),                                   # T5 K256 N96
+    ("d0", dict(T=37, K=384, N=144)),             # odd K-step count, partial row tile
+    ("d0", dict(T=130, K=256, N=272)),            # two token tiles (ragged), three row tiles
+    ("d0", dict(T=1, K=128, N=16)),               # smallest
+]
+
+
+@pytest.mark.parametrize("cfg,over", SMALL, ids=["d0", "T37K384N144", "T130K256N272", "T1K128N16"])
+@pytest.mark.parametrize("flags", [0, DEC, PRE], ids=["auto", "decode", "prefill"])
+def test_dense_small(cfg, over, flags, dev):
+    c = get_dense(cfg, dev, **over)
+    log(f"[dense] {cfg} {over} flags={flags}")
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    assert np.array_equal(xq.cpu().numpy(), c.xq) and np.array_equal(xs.cpu().numpy(), c.xs)
+    y = moe.dense_forward(c.dw, xq, xs, flags)
+    torch.cuda.synchronize()
+    toks = np.arange(c.sh.T, dtype=np.int32)
+    check_y(y.float().cpu().numpy(), c.ref(toks), f"dense/{over or cfg}/f{flags}")
+
+
+@pytest.mark.parametrize("cfg,ntok", [("d1", 8), ("d3", 16)])
+def test_dense_full_size(cfg, ntok, dev):
+    c = get_dense(cfg, dev)
+    log(f"[dense] {cfg} full size")
+    y = moe.dense_layer(c.dw, c.x)
+    y_other = moe.dense_layer(c.dw, c.x, PRE) if c.sh.T <= 32 else None   # the other path
+    torch.cuda.synchronize()
+    toks = sample_tokens(c.sh.T, ntok, seed=13)
+    ref = c.ref(toks)
+    check_y(y.float().cpu().numpy()[toks], ref, f"dense/{cfg}")
+    if y_other is not None:
+        check_y(y_other.float().cpu().numpy()[toks], ref, f"dense/{cfg}/other-path")
+    y2 = moe.dense_layer(c.dw, c.x)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def _unpack(packed: np.ndarray, N: int, K: int):
+    J = K // 128
+    ntl = N // 16
+    tiles = packed[:ntl * J * 2048].reshape(ntl, J, 2, 4, 16, 16)   # nt j half g r byte
+    s_off = (ntl * J * 2048 + 255) // 256 * 256
+    sc = packed[s_off:s_off + ntl * J * 64].reshape(ntl, J, 4, 16)    # nt j g r
+    wq = np.empty((N, K), dtype=np.uint8)
+    ws = np.empty((N, K // 32), dtype=np.uint8)
+    for half in range(2):
+        v = tiles[:, :, half].transpose(0, 3, 1, 2, 4)              # nt r j g byte
+        for g in range(4):
+            cols = np.arange(J)[:, None] * 128 + 64 * half + 16 * g + np.arange(16)[None, :]
+            wq.reshape(ntl, 16, K)[:, :, cols] = v[:, :, :, g, :]
+    ws[:] = sc.transpose(0, 3, 1, 2).reshape(N, K // 32)
+    return wq, ws
+
+
+def test_dense_prepack_roundtrip(dev):
+    c = get_dense("d0", dev, T=3, K=384, N=48)
+    wq, ws = _unpack(c.dw.buffer.cpu().numpy(), 48, 384)
+    assert np.array_equal(wq, c.inp.wq)
+    assert np.array_equal(ws, c.inp.ws)
+
+
+@pytest.mark.parametrize("flags", [DEC, PRE], ids=["decode", "prefill"])
+def test_dense_one_hot_is_exact(flags, dev):
+    T, K, N = 40, 384, 80
+    inp = synth.make_dense_inputs("d0", T=T, K=K, N=N)
+    wq = np.zeros((N, K), dtype=np.uint8)
+    cols = (13 * np.arange(N) + 7) % K
+    wq[np.arange(N), cols] = 0x38                       # +1.0
+    ws = np.full((N, K // 32), 127, dtype=np.uint8)     # 2^0
+    dw = moe.dense_prepack(to_dev(wq, dev), to_dev(ws, dev))
+    x = to_dev(inp.x.view(np.int16), dev).view(torch.bfloat16)
+    y = moe.dense_layer(dw, x, flags).float().cpu().numpy()
+    xq, xs = oracle.quant_mxfp8_bf16(inp.x)
+    want = oracle.decode_mxfp8(xq, xs)[:, cols]         # 4 significant bits: exact in bf16
+    assert np.array_equal(y, want.astype(np.float32))
