@@ -178,18 +178,24 @@ struct PackedLayout {
 // ------------------------------------------------- FP8 dense weight layout
 // Tile (nt, j): weight rows 16 nt .. +16, K 128 j .. +128, 2 KiB in the e4m3
 // MFMA operand's lane order (lane l = 16 g + r: row r, K [16 g, +16) in the
-// first KiB, K [64 + 16 g, +16) in the second); tiles of one row group are
-// consecutive along K.  Scales: 64 bytes per tile, byte l = row r, block g.
+// first KiB, K [64 + 16 g, +16) in the second).  The two tiles of a 32-row
+// group sit side by side for each K-step (4 KiB), and a group's K-steps are
+// consecutive.  Scales: 64 bytes per tile, byte l = row r, block g, grouped
+// the same way (128 bytes per group and K-step).
 struct DenseLayout {
   int N, K, J;
   size_t s_off, total;
+  static constexpr size_t kTileStep = 4096;   // bytes from K-step j to j + 1 of a tile
+  static constexpr size_t kScaleStep = 128;   // the same for its scales
   __host__ __device__ DenseLayout(int N_, int K_) : N(N_), K(K_), J(K_ / 128) {
     s_off = PackedLayout::align256((size_t)(N / 16) * J * 2048);
     total = PackedLayout::align256(s_off + (size_t)(N / 16) * J * 64);
   }
-  __host__ __device__ size_t tile_off(int nt, int j) const { return ((size_t)nt * J + j) * 2048; }
+  __host__ __device__ size_t tile_off(int nt, int j) const {
+    return ((size_t)(nt >> 1) * J + j) * kTileStep + (size_t)(nt & 1) * 2048;
+  }
   __host__ __device__ size_t scale_off(int nt, int j) const {
-    return s_off + ((size_t)nt * J + j) * 64;
+    return s_off + ((size_t)(nt >> 1) * J + j) * kScaleStep + (size_t)(nt & 1) * 64;
   }
 };
 

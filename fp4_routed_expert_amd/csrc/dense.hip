@@ -13,13 +13,16 @@
 // [16 g, 16 g + 16) in the first KiB and [64 + 16 g, +16) in the second (the
 // e4m3 operand layout measured on gfx950), so a wave loads a tile with two
 // fully contiguous 1 KiB runs; its 64 scale bytes follow the same lanes (lane
-// l: row r, 32-block g).  Tiles of one row group are consecutive along K.
+// l: row r, 32-block g).  The two tiles of a 32-row group are adjacent for
+// each K-step, and a group's K-steps are consecutive.
 //
-// Decode (few tokens): weight streaming.  A workgroup owns one 16-row group
-// and one 16-token tile; its waves split K and each keeps a batch of tiles in
-// flight; partial sums meet in LDS in wave order.  Prefill: LDS-tiled GEMM,
-// 128 tokens x 128 rows per workgroup, 128 K per stage, two register sets so
-// that one stage loads while another multiplies.
+// Decode (few tokens): weight streaming.  A workgroup owns one 32-row group
+// (two tiles, so each activation fragment serves two MFMAs) and one 16-token
+// tile; its 16 waves take the K-steps in turn (wave w: steps w, w + 16, ...),
+// so at any moment they read neighbouring 4 KiB blocks, each keeping two steps
+// in flight; partial sums meet in LDS in wave order.  Prefill: LDS-tiled
+// GEMM, 128 tokens x 128 rows per workgroup, 128 K per stage, two register
+// sets so that one stage loads while another multiplies.
 #include "common.h"
 
 namespace moe {
@@ -57,25 +60,45 @@ __global__ __launch_bounds__(256) void dense_pack_kernel(const uint8_t* __restri
 }
 
 // ------------------------------------------------------------------ decode
-// One K-step of a wave: the weight tile, its scale byte, the activation
+// One K-step of a wave: NT weight tiles and their scale bytes, the activation
 // fragment (token row r, the same two 16-byte pieces) and its scale byte.
+template <int NT>
 struct DStep {
-  v4u b0, b1, a0, a1;
-  uint32_t sb, sa;
+  v4u b0[NT], b1[NT], a0, a1;
+  uint32_t sb[NT], sa;
 };
 
-__device__ __forceinline__ void dload(DStep& s, const uint8_t* wt, const uint8_t* st,
-                                      const uint8_t* arow, const uint8_t* as, int j) {
-  const uint8_t* w = wt + (size_t)j * 2048;
-  s.b0 = *reinterpret_cast<const v4u*>(w);
-  s.b1 = *reinterpret_cast<const v4u*>(w + 1024);
-  s.sb = st[(size_t)j * 64];
+// wt[t]/st[t]: this lane's bytes of tile (nt0 + t, 0) and its scale; K-step j
+// is kTileStep * j further (scales: kScaleStep * j).
+template <int NT>
+__device__ __forceinline__ void dload(DStep<NT>& s, const uint8_t* const (&wt)[NT],
+                                      const uint8_t* const (&st)[NT], const uint8_t* arow,
+                                      const uint8_t* as, int j) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint8_t* w = wt[t] + (size_t)j * DenseLayout::kTileStep;
+    s.b0[t] = *reinterpret_cast<const v4u*>(w);
+    s.b1[t] = *reinterpret_cast<const v4u*>(w + 1024);
+    s.sb[t] = st[t][(size_t)j * DenseLayout::kScaleStep];
+  }
   s.a0 = *reinterpret_cast<const v4u*>(arow + (size_t)j * 128);
   s.a1 = *reinterpret_cast<const v4u*>(arow + (size_t)j * 128 + 64);
   s.sa = as[(size_t)j * 4];
 }
 
-template <int NW, int kB>
+template <int NT>
+__device__ __forceinline__ void dmma(const DStep<NT>& s, v4f (&acc)[NT]) {
+  const v8i a = cat8(s.a0, s.a1);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    acc[t] = mfma_fp8_fp8(a, cat8(s.b0[t], s.b1[t]), acc[t], (int)s.sa, (int)s.sb[t]);
+}
+
+// NW waves split the K-steps: with kIlv wave w takes steps w, w + NW, ...
+// (the workgroup's waves read neighbouring tiles at any moment), else one
+// contiguous range each.  NT row tiles per workgroup share each activation
+// fragment.
+template <int NW, int kB, int NT, bool kIlv>
 __global__ __launch_bounds__(64 * NW) void dense_decode_kernel(const uint8_t* __restrict__ packed,
                                                                const uint8_t* __restrict__ xq,
                                                                const uint8_t* __restrict__ xs,
@@ -84,48 +107,69 @@ __global__ __launch_bounds__(64 * NW) void dense_decode_kernel(const uint8_t* __
   const DenseLayout L(N, K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int nt = blockIdx.x, mt = blockIdx.y;
+  const int nt0 = blockIdx.x * NT, mt = blockIdx.y;
+  const int ntiles = N / 16;
   const int J = L.J;
-  const int j0 = (wave * J) / NW, j1 = ((wave + 1) * J) / NW;
-  // this lane's pieces: weight tile lane offset, activation row 16 mt + r
-  // (clamped: rows past T are computed from the last row and never stored)
-  const uint8_t* wt = packed + L.tile_off(nt, 0) + lane * 16;
-  const uint8_t* st = packed + L.scale_off(nt, 0) + lane;
+  // step u of this wave is K-step js + jstep * u, u < nsteps
+  int js, jstep, nsteps;
+  if (kIlv) {
+    js = wave;
+    jstep = NW;
+    nsteps = J > wave ? (J - wave + NW - 1) / NW : 0;
+  } else {
+    js = (wave * J) / NW;
+    jstep = 1;
+    nsteps = ((wave + 1) * J) / NW - js;
+  }
+  // this lane's pieces: weight tile lane offset (tiles past N clamped to the
+  // last one, never stored), activation row 16 mt + r (clamped the same way)
+  const uint8_t* wt[NT];
+  const uint8_t* st[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int ntc = min(nt0 + t, ntiles - 1);
+    wt[t] = packed + L.tile_off(ntc, 0) + lane * 16;
+    st[t] = packed + L.scale_off(ntc, 0) + lane;
+  }
   const int trow = min(16 * mt + r, T - 1);
   const uint8_t* arow = xq + (size_t)trow * K + 16 * g;
   const uint8_t* as = xs + (size_t)trow * (K / 32) + g;
 
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  DStep s[kB];
-  int j = j0;
+  v4f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  DStep<NT> s[kB];
+  int u = 0;
   // whole batches: kB steps' loads back to back, then their MFMAs
-  for (; j + kB <= j1; j += kB) {
+  for (; u + kB <= nsteps; u += kB) {
 #pragma unroll
-    for (int u = 0; u < kB; ++u) dload(s[u], wt, st, arow, as, j + u);
+    for (int b = 0; b < kB; ++b) dload<NT>(s[b], wt, st, arow, as, js + jstep * (u + b));
 #pragma unroll
-    for (int u = 0; u < kB; ++u)
-      acc = mfma_fp8_fp8(cat8(s[u].a0, s[u].a1), cat8(s[u].b0, s[u].b1), acc, (int)s[u].sa,
-                         (int)s[u].sb);
+    for (int b = 0; b < kB; ++b) dmma<NT>(s[b], acc);
   }
-  for (; j < j1; ++j) {
-    dload(s[0], wt, st, arow, as, j);
-    acc = mfma_fp8_fp8(cat8(s[0].a0, s[0].a1), cat8(s[0].b0, s[0].b1), acc, (int)s[0].sa,
-                       (int)s[0].sb);
+  for (; u < nsteps; ++u) {
+    dload<NT>(s[0], wt, st, arow, as, js + jstep * u);
+    dmma<NT>(s[0], acc);
   }
 
   // fixed-order sum of the waves' partials, then bf16 stores of the valid tokens
-  __shared__ v4f red[NW][64];
-  red[wave][lane] = acc;
+  __shared__ v4f red[NW][NT][64];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
   if (wave != 0) return;
-  v4f a = red[0][lane];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) a += red[w][lane];
-  const int n = 16 * nt + r;  // D column = weight row
+  for (int t = 0; t < NT; ++t) {
+    if (nt0 + t >= ntiles) break;
+    v4f a = red[0][t][lane];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int t = 16 * mt + 4 * g + v;  // D row = token
-    if (t < T) y[(size_t)t * N + n] = f32_to_bf16(a[v]);
+    for (int w = 1; w < NW; ++w) a += red[w][t][lane];
+    const int n = 16 * (nt0 + t) + r;  // D column = weight row
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tk = 16 * mt + 4 * g + v;  // D row = token
+      if (tk < T) y[(size_t)tk * N + n] = f32_to_bf16(a[v]);
+    }
   }
 }
 
@@ -162,7 +206,8 @@ __device__ __forceinline__ void dense_gload(DLoad& d, const uint8_t* __restrict_
   for (int i = 0; i < 4; ++i) d.a[i] = *reinterpret_cast<const v4u*>(xq + (g.a[i] + 128u * jj)) & live;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    d.b[i] = *reinterpret_cast<const v4u*>(packed + (g.b[i] + 2048u * jj)) & live;
+    d.b[i] = *reinterpret_cast<const v4u*>(packed + (g.b[i] + (uint32_t)DenseLayout::kTileStep * jj)) &
+             live;
   d.sc = *reinterpret_cast<const uint32_t*>(g.sbase + (g.soff + g.sstep * jj));
 }
 
@@ -238,7 +283,7 @@ __global__ __launch_bounds__(256) void dense_prefill_kernel(const uint8_t* __res
   } else {
     src.sbase = packed;
     src.soff = (uint32_t)L.scale_off(min(nt0 + ((tid - 128) >> 4), ntiles - 1), 0) + 4 * (tid & 15);
-    src.sstep = 64;
+    src.sstep = (uint32_t)DenseLayout::kScaleStep;
   }
 
   v4f acc[4][4];
@@ -297,8 +342,11 @@ hipError_t launch_dense_pack(const uint8_t* wq, const uint8_t* ws, int N, int K,
 
 hipError_t launch_dense_decode(const uint8_t* packed, const uint8_t* xq, const uint8_t* xs, int T,
                                int N, int K, uint16_t* y, hipStream_t s) {
-  const dim3 grid((unsigned)(N / 16), (unsigned)((T + 15) / 16));
-  hipLaunchKernelGGL((dense_decode_kernel<8, 4>), grid, dim3(512), 0, s, packed, xq, xs, T, N, K, y);
+  constexpr int kNW = 16, kBt = 2, kNT = 2;
+  constexpr bool kIl = true;
+  const dim3 grid((unsigned)((N / 16 + kNT - 1) / kNT), (unsigned)((T + 15) / 16));
+  hipLaunchKernelGGL((dense_decode_kernel<kNW, kBt, kNT, kIl>), grid, dim3(64 * kNW), 0, s, packed,
+                     xq, xs, T, N, K, y);
   return hipGetLastError();
 }
 

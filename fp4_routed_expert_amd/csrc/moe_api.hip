@@ -532,7 +532,7 @@ extern "C" {
 
 static moe_status_t check_dense_nk(int32_t N, int32_t K) {
   if (N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
-  if (N % 16 != 0 || K % 128 != 0 || N > (1 << 20) || K > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  if (N % 32 != 0 || K % 128 != 0 || N > (1 << 20) || K > (1 << 20)) return MOE_ERR_UNSUPPORTED;
   if (DenseLayout(N, K).total >= ((size_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -322,7 +322,7 @@ moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/, i
  * moe_fp8_dense_prepack: wq [N, K] e4m3 codes (16-byte aligned), ws [N, K/32]
  * E8M0 -> `packed` (device, >= moe_fp8_dense_packed_bytes(N, K) bytes,
  * 256-byte aligned) in the kernels' tile order, and `desc` (host), as for the
- * expert weights.  N % 16 == 0, K % 128 == 0, packed size < 4 GiB.
+ * expert weights.  N % 32 == 0, K % 128 == 0, packed size < 4 GiB.
  *
  * moe_fp8_dense_forward: xq [T, K] (16-byte aligned), xs [T, K/32] (4-byte
  * aligned), y [T, N] bf16 bits (out).  T * K < 2^32.  Path: weight streaming

@@ -201,7 +201,7 @@ def test_router_and_shared_argument_errors():
 def test_dense_argument_errors():
     nb = L.moe_fp8_dense_packed_bytes(7168, 16384)
     assert 7168 * 16384 * (1 + 1 / 32) <= nb <= 7168 * 16384 * (1 + 1 / 32) + 512
-    assert L.moe_fp8_dense_packed_bytes(100, 256) == 0         # N % 16
+    assert L.moe_fp8_dense_packed_bytes(112, 256) == 0         # N % 32
     assert L.moe_fp8_dense_packed_bytes(96, 200) == 0          # K % 128
     d = _lib.MoeFp8DenseWeights()
     pre = L.moe_fp8_dense_prepack

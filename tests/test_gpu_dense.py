@@ -48,13 +48,13 @@ def get_dense(key, dev, **over):
 
 SMALL = [
     ("d0", {}),                                   # T5 K256 N96
-    ("d0", dict(T=37, K=384, N=144)),             # odd K-step count, partial row tile
-    ("d0", dict(T=130, K=256, N=272)),            # two token tiles (ragged), three row tiles
-    ("d0", dict(T=1, K=128, N=16)),               # smallest
+    ("d0", dict(T=37, K=384, N=160)),             # odd K-step count, partial row tile
+    ("d0", dict(T=130, K=256, N=288)),            # two token tiles (ragged), three row tiles
+    ("d0", dict(T=1, K=128, N=32)),               # smallest
 ]
 
 
-@pytest.mark.parametrize("cfg,over", SMALL, ids=["d0", "T37K384N144", "T130K256N272", "T1K128N16"])
+@pytest.mark.parametrize("cfg,over", SMALL, ids=["d0", "T37K384N160", "T130K256N288", "T1K128N32"])
 @pytest.mark.parametrize("flags", [0, DEC, PRE], ids=["auto", "decode", "prefill"])
 def test_dense_small(cfg, over, flags, dev):
     c = get_dense(cfg, dev, **over)
@@ -85,32 +85,34 @@ def test_dense_full_size(cfg, ntok, dev):
 
 
 def _unpack(packed: np.ndarray, N: int, K: int):
+    """Read the packed layout back: per 32-row group and K-step, 2 tiles of 2 KiB
+    (lane l = 16 g + r: row r, K [16 g, +16) then K [64 + 16 g, +16)), then the
+    scales, 64 bytes per tile in the same grouping."""
     J = K // 128
-    ntl = N // 16
-    tiles = packed[:ntl * J * 2048].reshape(ntl, J, 2, 4, 16, 16)   # nt j half g r byte
-    s_off = (ntl * J * 2048 + 255) // 256 * 256
-    sc = packed[s_off:s_off + ntl * J * 64].reshape(ntl, J, 4, 16)    # nt j g r
+    ng = N // 32
+    tiles = packed[:ng * J * 4096].reshape(ng, J, 2, 2, 4, 16, 16)   # grp j tile half g r byte
+    s_off = (ng * J * 4096 + 255) // 256 * 256
+    sc = packed[s_off:s_off + ng * J * 128].reshape(ng, J, 2, 4, 16)   # grp j tile g r
     wq = np.empty((N, K), dtype=np.uint8)
-    ws = np.empty((N, K // 32), dtype=np.uint8)
+    w4 = wq.reshape(ng, 2, 16, K)                                      # grp tile r K
     for half in range(2):
-        v = tiles[:, :, half].transpose(0, 3, 1, 2, 4)              # nt r j g byte
         for g in range(4):
             cols = np.arange(J)[:, None] * 128 + 64 * half + 16 * g + np.arange(16)[None, :]
-            wq.reshape(ntl, 16, K)[:, :, cols] = v[:, :, :, g, :]
-    ws[:] = sc.transpose(0, 3, 1, 2).reshape(N, K // 32)
+            w4[:, :, :, cols] = tiles[:, :, :, half, g].transpose(0, 2, 3, 1, 4)   # grp tile r j byte
+    ws = sc.transpose(0, 2, 4, 1, 3).reshape(N, K // 32)               # grp tile r j g
     return wq, ws
 
 
 def test_dense_prepack_roundtrip(dev):
-    c = get_dense("d0", dev, T=3, K=384, N=48)
-    wq, ws = _unpack(c.dw.buffer.cpu().numpy(), 48, 384)
+    c = get_dense("d0", dev, T=3, K=384, N=64)
+    wq, ws = _unpack(c.dw.buffer.cpu().numpy(), 64, 384)
     assert np.array_equal(wq, c.inp.wq)
     assert np.array_equal(ws, c.inp.ws)
 
 
 @pytest.mark.parametrize("flags", [DEC, PRE], ids=["decode", "prefill"])
 def test_dense_one_hot_is_exact(flags, dev):
-    T, K, N = 40, 384, 80
+    T, K, N = 40, 384, 96
     inp = synth.make_dense_inputs("d0", T=T, K=K, N=N)
     wq = np.zeros((N, K), dtype=np.uint8)
     cols = (13 * np.arange(N) + 7) % K
