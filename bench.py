@@ -40,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true>"   # the instantiation the library launches
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 (and FP8 x FP4 scaled MFMA at the FP8 issue rate)
 METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU"
 
@@ -90,6 +91,8 @@ def rocprof_summary(paths) -> str:
 KERNEL_SOURCES = {
     "up_decode_kernel": "fp4_routed_expert_amd/csrc/expert_decode.hip",
     "prefill_gemm_kernel<true>": "fp4_routed_expert_amd/csrc/expert_prefill.hip",
+    DENSE_DECODE_KERNEL: "fp4_routed_expert_amd/csrc/dense.hip",
+    "dense_prefill_kernel": "fp4_routed_expert_amd/csrc/dense.hip",
 }
 
 
@@ -274,16 +277,21 @@ def bench_dense(args):
     decode = args.flags == 1 or (args.flags == 0 and T <= 32)
     b_alg = N * K * (1 + 1 / 32) + T * K * (1 + 1 / 32) + T * N * 2
     f_alg = 2.0 * T * N * K
+    wl = synth.DENSE_NAMES.get(args.config, args.config)
     if decode:
         ach = b_alg / (k_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "dense_decode_kernel (FP8 weight streaming)", "achieved": ach,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+        roof = {"bound": "hbm", "kernel": DENSE_DECODE_KERNEL + " (FP8 weight streaming)", "achieved": ach,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": load_traffic(DENSE_DECODE_KERNEL, wl),
                 "alg_bytes_per_launch": b_alg, "avg_launch_us": k_ms * 1e3}
     else:
         ach = f_alg / (k_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "dense_prefill_kernel (LDS-tiled FP8 GEMM)", "achieved": ach,
                 "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_FP8_PEAK_TFLOPS,
-                "traffic": None, "alg_flops_per_launch": f_alg, "avg_launch_us": k_ms * 1e3}
+                "traffic": load_traffic("dense_prefill_kernel", wl),
+                "alg_flops_per_launch": f_alg, "avg_launch_us": k_ms * 1e3}
+    if args.copy_calibration:
+        copy_calibration()
     ms = dt / args.steps * 1e3
     line = {
         "metric": "FP8 dense projection tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU",

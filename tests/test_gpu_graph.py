@@ -61,3 +61,48 @@ def test_layer_graph_replays_match_eager(shape, flags, dev):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, expected), f"replay {rep} differs from eager"
+
+
+def test_full_layer_and_dense_graph_replays_match_eager(dev):
+    """The layer from hidden states (router slice planes in the workspace, one
+    shared expert) and the FP8 dense projection, captured and replayed with new
+    inputs between replays; every replay equals an eager call bit for bit."""
+    c = get_case("c1", dev)
+    sh = c.sh
+    names = ("w1", "s1", "w3", "s3", "w2", "s2")
+    sw = synth.make_shared_weights(sh)
+    pw = moe.prepack_weights(*[torch.from_numpy(np.concatenate([getattr(c.inp, n), sw[i]])).to(dev)
+                               for i, n in enumerate(names)])
+    wg = torch.from_numpy(synth.make_router_weights(sh).view(np.int16)).to(dev).view(torch.bfloat16)
+    dn = synth.make_dense_inputs("d0", T=sh.T, K=sh.H, N=96)
+    dw = moe.dense_prepack(torch.from_numpy(dn.wq).to(dev), torch.from_numpy(dn.ws).to(dev))
+    x_buf = c.x.clone()
+    y = torch.empty((sh.T, sh.H), dtype=torch.float32, device=dev)
+    yd = torch.empty((sh.T, 96), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((sh.T, sh.H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((sh.T, sh.H // 32), dtype=torch.uint8, device=dev)
+    ws = torch.empty(moe.layer_full_workspace_size(sh.T, sh.k, sh.E + 1, sh.H, sh.I, 1),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        moe.layer_forward_full(pw, 1, wg, x_buf, sh.k, y=y, workspace=ws)
+        moe.quant_act_mxfp8(x_buf, xq, xs)
+        moe.dense_forward(dw, xq, xs, y=yd)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        x_buf.copy_(torch.roll(c.x, shifts=rep + 1, dims=0))
+        want_y = moe.layer_forward_full(pw, 1, wg, x_buf, sh.k)
+        want_d = moe.dense_layer(dw, x_buf)
+        torch.cuda.synchronize()
+        y.fill_(float("nan"))
+        yd.fill_(0)
+        ws.fill_(0x77)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want_y), f"full layer replay {rep} differs from eager"
+        assert torch.equal(yd.view(torch.int16), want_d.view(torch.int16)), f"dense replay {rep}"
