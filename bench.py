@@ -40,7 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true>"   # the instantiation the library launches
+DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true>"   # the instantiations the library launches
+DENSE_PREFILL_KERNEL = "dense_prefill_kernel<2, 4, 6, 2>"     # (prefill: from 256 tokens)
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 (and FP8 x FP4 scaled MFMA at the FP8 issue rate)
 METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU"
 
@@ -92,7 +93,7 @@ KERNEL_SOURCES = {
     "up_decode_kernel": "fp4_routed_expert_amd/csrc/expert_decode.hip",
     "prefill_gemm_kernel<true>": "fp4_routed_expert_amd/csrc/expert_prefill.hip",
     DENSE_DECODE_KERNEL: "fp4_routed_expert_amd/csrc/dense.hip",
-    "dense_prefill_kernel": "fp4_routed_expert_amd/csrc/dense.hip",
+    DENSE_PREFILL_KERNEL: "fp4_routed_expert_amd/csrc/dense.hip",
 }
 
 
@@ -286,9 +287,9 @@ def bench_dense(args):
                 "alg_bytes_per_launch": b_alg, "avg_launch_us": k_ms * 1e3}
     else:
         ach = f_alg / (k_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "dense_prefill_kernel (LDS-tiled FP8 GEMM)", "achieved": ach,
+        roof = {"bound": "mfma", "kernel": DENSE_PREFILL_KERNEL + " (LDS-tiled FP8 GEMM)", "achieved": ach,
                 "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_FP8_PEAK_TFLOPS,
-                "traffic": load_traffic("dense_prefill_kernel", wl),
+                "traffic": load_traffic(DENSE_PREFILL_KERNEL, wl),
                 "alg_flops_per_launch": f_alg, "avg_launch_us": k_ms * 1e3}
     if args.copy_calibration:
         copy_calibration()

@@ -174,145 +174,183 @@ __global__ __launch_bounds__(64 * NW) void dense_decode_kernel(const uint8_t* __
 }
 
 // ----------------------------------------------------------------- prefill
-constexpr int kDB = 128;                        // tokens and weight rows per tile
-constexpr int kDA = kDB * 128;                  // A bytes per stage (128 rows x 128 K)
-constexpr int kDBw = 8 * 2048;                  // B bytes per stage (8 packed tiles)
-constexpr int kDStage = kDA + kDBw + 512 + 512;  // + A scales (dword per row) + B scales
+// Tile geometry: kWM x kWN waves, each owning kSM 16-token sub-tiles x 4
+// weight tiles (64 rows); the workgroup tile is BM tokens x 16 BT weight rows.
+// Per stage of 128 K the LDS holds A = BM x-rows (128 bytes each, swizzled),
+// B = BT packed weight tiles, then one dword per thread: the scale dwords of
+// the BM x rows, the 16 BT 4-byte runs of weight-tile scales, padding.
+template <int kWM, int kWN, int kSM>
+struct DCfg {
+  static constexpr int NT = 64 * kWM * kWN;
+  static constexpr int BM = kWM * 16 * kSM;
+  static constexpr int BT = kWN * 4;
+  static constexpr int A = BM * 128;
+  static constexpr int B = BT * 2048;
+  static constexpr int SA = BM * 4;
+  static constexpr int STAGE = A + B + 4 * NT;
+  static constexpr int RA = BM * 8 / NT;    // 16-byte x chunks per thread and stage
+  static constexpr int RB = BT * 128 / NT;  // 16-byte weight chunks per thread and stage
+  static_assert(BM + 16 * BT <= NT, "one scale dword per thread at most");
+  static_assert(RA * NT == BM * 8 && RB * NT == BT * 128, "whole rounds of chunks");
+};
 
+template <class C>
 struct DLoad {
-  v4u a[4], b[4];
-  uint32_t sc;  // threads < 128: x row tid's scale dword; others: a weight tile's scale dword
+  v4u a[C::RA], b[C::RB];
+  uint32_t sc;  // threads < BM: x row tid's scale dword; others: 4 scale bytes of a weight tile
 };
 
 __device__ __forceinline__ int dswz(int row, int q) { return row * 128 + ((q ^ (row & 7)) << 4); }
 
-// Global sources of one thread for the stage at K-step j: 4 x rows (32 apart)
-// at granule lq, 4 16-byte chunks of the weight tiles btile + 2 i, and (threads
-// below 128) the scale dwords of x row tid and of weight tile tid >> 4.
+// Global sources of one thread at K-step 0 (byte offsets, all < 2^32): x rows
+// (tid >> 3) + (NT / 8) i at granule tid & 7; 16 bytes (tid & 127) of weight
+// tiles (tid >> 7) + (NT / 128) i; one scale dword.
+template <class C>
 struct DSrc {
-  uint32_t a[4], b[4];     // byte offsets from xq and packed (all < 2^32)
-  const uint8_t* sbase;    // xs (threads < 128) or packed
+  uint32_t a[C::RA], b[C::RB];
+  const uint8_t* sbase;    // xs (threads < BM) or packed
   uint32_t soff, sstep;    // scale dword offset at K-step 0, bytes per K-step
 };
 
 // Loads K-step min(j, J - 1); a step j >= J (the padding step of an odd
 // count) is zeroed instead, so its products are exact zeros.
-__device__ __forceinline__ void dense_gload(DLoad& d, const uint8_t* __restrict__ xq,
-                                            const uint8_t* __restrict__ packed, const DSrc& g,
+template <class C>
+__device__ __forceinline__ void dense_gload(DLoad<C>& d, const uint8_t* __restrict__ xq,
+                                            const uint8_t* __restrict__ packed, const DSrc<C>& g,
                                             int j, int J) {
   const uint32_t live = j < J ? ~0u : 0u;  // uniform: a mask, not a branch
   const uint32_t jj = (uint32_t)min(j, J - 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) d.a[i] = *reinterpret_cast<const v4u*>(xq + (g.a[i] + 128u * jj)) & live;
+  for (int i = 0; i < C::RA; ++i)
+    d.a[i] = *reinterpret_cast<const v4u*>(xq + (g.a[i] + 128u * jj)) & live;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::RB; ++i)
     d.b[i] = *reinterpret_cast<const v4u*>(packed + (g.b[i] + (uint32_t)DenseLayout::kTileStep * jj)) &
              live;
   d.sc = *reinterpret_cast<const uint32_t*>(g.sbase + (g.soff + g.sstep * jj));
 }
 
-// LDS stage: A rows (swizzled) | 8 weight tiles | 128 A scale dwords | 128 B
-// scale dwords (thread tid writes dword tid of the last two).
-__device__ __forceinline__ void dense_lstore(const DLoad& d, uint8_t* buf, int lr, int lq,
-                                             int boff, int tid) {
+template <class C>
+__device__ __forceinline__ void dense_lstore(const DLoad<C>& d, uint8_t* buf, int tid) {
+  const int lr = tid >> 3, lq = tid & 7;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(buf + dswz(32 * i + lr, lq)) = d.a[i];
+  for (int i = 0; i < C::RA; ++i)
+    *reinterpret_cast<v4u*>(buf + dswz(C::NT / 8 * i + lr, lq)) = d.a[i];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(buf + kDA + boff + 4096 * i) = d.b[i];
-  *reinterpret_cast<uint32_t*>(buf + kDA + kDBw + 4 * tid) = d.sc;
+  for (int i = 0; i < C::RB; ++i)
+    *reinterpret_cast<v4u*>(buf + C::A + ((tid >> 7) + C::NT / 128 * i) * 2048 + 16 * (tid & 127)) =
+        d.b[i];
+  *reinterpret_cast<uint32_t*>(buf + C::A + C::B + 4 * tid) = d.sc;
 }
 
-// One stage's 16 MFMAs of a wave (4 token sub-tiles x 4 weight tiles).
-__device__ __forceinline__ void dense_compute(v4f (&acc)[4][4], const uint8_t* cur, int wm, int wn,
-                                              int lane) {
+// One stage's 4 kSM MFMAs of a wave (kSM token sub-tiles x 4 weight tiles).
+template <class C, int kSM>
+__device__ __forceinline__ void dense_compute(v4f (&acc)[kSM][4], const uint8_t* cur, int wm,
+                                              int wn, int lane) {
   const int r = lane & 15, g = lane >> 4;
   v8i b[4];
   int sb[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint8_t* tb = cur + kDA + (4 * wn + t) * 2048 + 16 * lane;
+    const uint8_t* tb = cur + C::A + (4 * wn + t) * 2048 + 16 * lane;
     b[t] = cat8(*reinterpret_cast<const v4u*>(tb), *reinterpret_cast<const v4u*>(tb + 1024));
-    sb[t] = cur[kDA + kDBw + 512 + (4 * wn + t) * 64 + lane];
+    sb[t] = cur[C::A + C::B + C::SA + (4 * wn + t) * 64 + lane];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 64 * wm + 16 * i + r;
+  for (int i = 0; i < kSM; ++i) {
+    const int row = 16 * kSM * wm + 16 * i + r;
     const v8i a = cat8(*reinterpret_cast<const v4u*>(cur + dswz(row, g)),
                        *reinterpret_cast<const v4u*>(cur + dswz(row, 4 + g)));
-    const int sa = cur[kDA + kDBw + 4 * row + g];
+    const int sa = cur[C::A + C::B + 4 * row + g];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = mfma_fp8_fp8(a, b[t], acc[i][t], sa, sb[t]);
   }
 }
 
-__global__ __launch_bounds__(256) void dense_prefill_kernel(const uint8_t* __restrict__ packed,
-                                                            const uint8_t* __restrict__ xq,
-                                                            const uint8_t* __restrict__ xs, int T,
-                                                            int N, int K,
-                                                            uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kDStage];
+template <int kWM, int kWN, int kSM, int kSets>
+__global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ xq,
+    const uint8_t* __restrict__ xs, int T, int N, int K, uint16_t* __restrict__ y) {
+  using C = DCfg<kWM, kWN, kSM>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
   const DenseLayout L(N, K);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int NTn = (N + kDB - 1) / kDB;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int NTn = (N + 16 * C::BT - 1) / (16 * C::BT);
   // weight-row tiles vary fastest: the token tile's x rows stay in L2 while its
   // row tiles go by, consecutive workgroups of an XCD (block % 8) share them
   const int bn = (int)(blockIdx.x % (unsigned)NTn), bm = (int)(blockIdx.x / (unsigned)NTn);
-  const int m0 = bm * kDB, nt0 = bn * 8;  // first 16-row weight tile
+  const int m0 = bm * C::BM, nt0 = bn * C::BT;  // first token, first 16-row weight tile
   const int ntiles = N / 16;
   const int J = L.J;
 
-  // global sources of this thread: 4 x rows (32 apart), granule lq; 4 chunks of
-  // the 8 weight tiles (tile (tid >> 7) + 2 i, 16 bytes (tid & 127)); the scale
-  // dwords of x row tid and of weight tile tid >> 4 (threads < 128)
-  const int lr = tid >> 3, lq = tid & 7;
-  const int btile = tid >> 7;  // chunk i covers weight tile btile + 2 i
-  const int boff = btile * 2048 + 16 * (tid & 127);
-  DSrc src;
+  DSrc<C> src;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) src.a[i] = (uint32_t)min(m0 + 32 * i + lr, T - 1) * (uint32_t)K + 16 * lq;
+  for (int i = 0; i < C::RA; ++i)
+    src.a[i] = (uint32_t)min(m0 + C::NT / 8 * i + (tid >> 3), T - 1) * (uint32_t)K + 16 * (tid & 7);
   // weight tiles past N are clamped to the last one (their columns are never
   // stored), so each chunk keeps its own base
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    src.b[i] = (uint32_t)L.tile_off(min(nt0 + btile + 2 * i, ntiles - 1), 0) + 16 * (tid & 127);
-  if (tid < 128) {
+  for (int i = 0; i < C::RB; ++i)
+    src.b[i] = (uint32_t)L.tile_off(min(nt0 + (tid >> 7) + C::NT / 128 * i, ntiles - 1), 0) +
+               16 * (tid & 127);
+  if (tid < C::BM) {
     src.sbase = xs;
     src.soff = (uint32_t)min(m0 + tid, T - 1) * (uint32_t)(K / 32);
     src.sstep = 4;
   } else {
+    // weight-tile scales; threads past the last run re-read tile run 0 into the padding
+    const int u = tid - C::BM < 16 * C::BT ? tid - C::BM : 0;
     src.sbase = packed;
-    src.soff = (uint32_t)L.scale_off(min(nt0 + ((tid - 128) >> 4), ntiles - 1), 0) + 4 * (tid & 15);
+    src.soff = (uint32_t)L.scale_off(min(nt0 + (u >> 4), ntiles - 1), 0) + 4 * (u & 15);
     src.sstep = (uint32_t)DenseLayout::kScaleStep;
   }
 
-  v4f acc[4][4];
+  v4f acc[kSM][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kSM; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Stage j + 2 loads while j multiplies and j + 1 goes to the idle buffer.
-  // The steps run in pairs; an odd count gets a zero padding step (a step
-  // left over after the loop would make the compiler rename the
-  // accumulators, doubling their registers).
+  // kSets = 2: stage j + 2 loads while j multiplies and j + 1 goes to the
+  // idle buffer; kSets = 1: stage j + 1 loads while j multiplies.  The steps
+  // run in pairs; an odd count gets a zero padding step (a step left over
+  // after the loop would make the compiler rename the accumulators, doubling
+  // their registers).
   const int J2 = J + (J & 1);
-  DLoad p, q;
-  dense_gload(p, xq, packed, src, 0, J);
-  dense_gload(q, xq, packed, src, 1, J);
-  dense_lstore(p, lds, lr, lq, boff, tid);
-  __syncthreads();
   uint8_t* const buf0 = lds;
-  uint8_t* const buf1 = lds + kDStage;
-  for (int j = 0; j < J2; j += 2) {
-    dense_gload(p, xq, packed, src, j + 2, J);
-    dense_compute(acc, buf0, wm, wn, lane);
-    dense_lstore(q, buf1, lr, lq, boff, tid);
+  uint8_t* const buf1 = lds + C::STAGE;
+  if constexpr (kSets == 2) {
+    DLoad<C> p, q;
+    dense_gload<C>(p, xq, packed, src, 0, J);
+    dense_gload<C>(q, xq, packed, src, 1, J);
+    dense_lstore<C>(p, lds, tid);
     __syncthreads();
-    dense_gload(q, xq, packed, src, j + 3, J);
-    dense_compute(acc, buf1, wm, wn, lane);
-    dense_lstore(p, buf0, lr, lq, boff, tid);
+    for (int j = 0; j < J2; j += 2) {
+      dense_gload<C>(p, xq, packed, src, j + 2, J);
+      dense_compute<C, kSM>(acc, buf0, wm, wn, lane);
+      dense_lstore<C>(q, buf1, tid);
+      __syncthreads();
+      dense_gload<C>(q, xq, packed, src, j + 3, J);
+      dense_compute<C, kSM>(acc, buf1, wm, wn, lane);
+      dense_lstore<C>(p, buf0, tid);
+      __syncthreads();
+    }
+  } else {
+    DLoad<C> p;
+    dense_gload<C>(p, xq, packed, src, 0, J);
+    dense_lstore<C>(p, lds, tid);
     __syncthreads();
+    for (int j = 0; j < J2; j += 2) {
+      dense_gload<C>(p, xq, packed, src, j + 1, J);
+      dense_compute<C, kSM>(acc, buf0, wm, wn, lane);
+      dense_lstore<C>(p, buf1, tid);
+      __syncthreads();
+      dense_gload<C>(p, xq, packed, src, j + 2, J);
+      dense_compute<C, kSM>(acc, buf1, wm, wn, lane);
+      dense_lstore<C>(p, buf0, tid);
+      __syncthreads();
+    }
   }
 
   const int r = lane & 15, g = lane >> 4;
@@ -321,14 +359,22 @@ __global__ __launch_bounds__(256) void dense_prefill_kernel(const uint8_t* __res
     const int n = 16 * (nt0 + 4 * wn + t) + r;
     if (n >= N) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kSM; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int tok = m0 + 64 * wm + 16 * i + 4 * g + v;
+        const int tok = m0 + 16 * kSM * wm + 16 * i + 4 * g + v;
         if (tok < T) y[(size_t)tok * N + n] = f32_to_bf16(acc[i][t][v]);
       }
   }
 }
+
+// the two geometries: 128 x 128 (4 waves) and, from 256 tokens, 192 x 256 (8 waves;
+// 256 x 256 does not fit 2 waves per SIMD without spills, 192 x 256 is 11 % faster than
+// 128 x 128 on 4604 tokens: fewer bytes staged per flop)
+constexpr int kLWM = 2, kLWN = 4, kLSM = 6, kLSets = 2;
+using DSmall = DCfg<2, 2, 4>;
+using DLarge = DCfg<kLWM, kLWN, kLSM>;
+constexpr int kDenseLargeMinT = 256;
 
 }  // namespace
 
@@ -352,9 +398,18 @@ hipError_t launch_dense_decode(const uint8_t* packed, const uint8_t* xq, const u
 
 hipError_t launch_dense_prefill(const uint8_t* packed, const uint8_t* xq, const uint8_t* xs, int T,
                                 int N, int K, uint16_t* y, hipStream_t s) {
-  const long blocks = (long)((T + kDB - 1) / kDB) * ((N + kDB - 1) / kDB);
-  hipLaunchKernelGGL(dense_prefill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, xq, xs,
-                     T, N, K, y);
+  if (T >= kDenseLargeMinT) {
+    const long blocks = (long)((T + DLarge::BM - 1) / DLarge::BM) *
+                        ((N + 16 * DLarge::BT - 1) / (16 * DLarge::BT));
+    hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets>), dim3((unsigned)blocks),
+                       dim3(DLarge::NT), 0, s,
+                       packed, xq, xs, T, N, K, y);
+  } else {
+    const long blocks = (long)((T + DSmall::BM - 1) / DSmall::BM) *
+                        ((N + 16 * DSmall::BT - 1) / (16 * DSmall::BT));
+    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2>), dim3((unsigned)blocks), dim3(DSmall::NT), 0, s,
+                       packed, xq, xs, T, N, K, y);
+  }
   return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 """GPU parity of the FP8 dense projection, through the C ABI.
 
 y (bf16) against the oracle's fp64 sums on the same MXFP8 rows, on both
-paths (weight streaming and the LDS-tiled GEMM): the tiny workload, ragged
+paths (weight streaming and the LDS-tiled GEMM, in both of its tile
+geometries): the tiny workload, ragged
 token counts, an odd K-step count (the tiled kernel's zero padding step),
 weight-row counts that leave a partial 128-row tile, the decode-shaped and
 prefill-shaped projections at full size (sampled tokens), plus the prepacked
@@ -51,10 +52,11 @@ SMALL = [
     ("d0", dict(T=37, K=384, N=160)),             # odd K-step count, partial row tile
     ("d0", dict(T=130, K=256, N=288)),            # two token tiles (ragged), three row tiles
     ("d0", dict(T=1, K=128, N=32)),               # smallest
+    ("d0", dict(T=300, K=384, N=288)),            # large-tile geometry: ragged tokens and rows, odd K-steps
 ]
 
 
-@pytest.mark.parametrize("cfg,over", SMALL, ids=["d0", "T37K384N160", "T130K256N288", "T1K128N32"])
+@pytest.mark.parametrize("cfg,over", SMALL, ids=["d0", "T37K384N160", "T130K256N288", "T1K128N32", "T300K384N288"])
 @pytest.mark.parametrize("flags", [0, DEC, PRE], ids=["auto", "decode", "prefill"])
 def test_dense_small(cfg, over, flags, dev):
     c = get_dense(cfg, dev, **over)
