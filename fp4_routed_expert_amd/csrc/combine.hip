@@ -14,6 +14,8 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint2* __restrict__ O,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ pair_pos,
@@ -38,7 +40,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint2* __restrict__ 
       g[u] = gates[idx];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = O[(size_t)row[u] * H4 + c];
+    for (int u = 0; u < 8; ++u) {
+      const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(O + (size_t)row[u] * H4 + c));
+      o[u] = make_uint2(w.x, w.y);
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float4 a = make_float4(fmaf(g[u], bf16_lo(o[u].x), acc.x), fmaf(g[u], bf16_hi(o[u].x), acc.y),
@@ -53,7 +58,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint2* __restrict__ 
     acc.z += bf16_lo(o.y);
     acc.w += bf16_hi(o.y);
   }
-  y[(size_t)t * H4 + c] = acc;
+  // O is read once and y written once per layer: non-temporal accesses
+  __builtin_nontemporal_store(v4f{acc.x, acc.y, acc.z, acc.w}, reinterpret_cast<v4f*>(y + (size_t)t * H4 + c));
 }
 
 }  // namespace

@@ -77,8 +77,9 @@ __device__ __forceinline__ void dload(DStep<NT>& s, const uint8_t* const (&wt)[N
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const uint8_t* w = wt[t] + (size_t)j * DenseLayout::kTileStep;
-    s.b0[t] = *reinterpret_cast<const v4u*>(w);
-    s.b1[t] = *reinterpret_cast<const v4u*>(w + 1024);
+    // weights are streamed once: non-temporal loads leave the caches to the activations
+    s.b0[t] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(w));
+    s.b1[t] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(w + 1024));
     s.sb[t] = st[t][(size_t)j * DenseLayout::kScaleStep];
   }
   s.a0 = *reinterpret_cast<const v4u*>(arow + (size_t)j * 128);

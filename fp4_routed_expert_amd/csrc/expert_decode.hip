@@ -42,6 +42,7 @@ namespace moe {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // The FP4 B operand occupies four registers; the builtin's operand is eight
 // wide, the upper half is never read for the e2m1 format.
@@ -83,7 +84,12 @@ template <int NT>
 __device__ __forceinline__ void load_step(Step<NT>& r, const Stream<NT>& st, int j) {
   const uint8_t* wj = st.w + (size_t)j * (NT * 1024);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) r.b[t] = *reinterpret_cast<const uint4*>(wj + t * 1024);
+  for (int t = 0; t < NT; ++t) {
+    // streamed once per step: a non-temporal load keeps them from displacing
+    // the activation rows in the caches
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wj + t * 1024));
+    r.b[t] = make_uint4(v.x, v.y, v.z, v.w);
+  }
   if constexpr (NT == 4)
     r.sw = *reinterpret_cast<const uint32_t*>(st.s + (size_t)j * 256);
   else
