@@ -11,6 +11,11 @@
  * ("DeepSeek-V4-Flash on AMD gfx90a: Correctness Recovery and Inference
  * Performance Engineering", abstract).
  *
+ * Around the layer: the router logits from the hidden states and shared
+ * experts (moe_router_logits, moe_fp4_layer_forward_full, the shared-expert
+ * stage calls), and the FP8 dense projections the same pages list beside the
+ * FP4 experts (moe_fp8_dense_*).
+ *
  * Conventions shared by every call:
  *  - Pointers are DEVICE pointers unless a comment says (host).  The caller
  *    allocates and frees everything, including workspaces sized by the
