@@ -307,6 +307,94 @@ def bench_dense(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_shard(args):
+    """One GPU's share of the layer: EP (the gate/up and down calls over experts
+    0..E/G-1 on the full routing's pairs) or TP (the whole layer call over the
+    intermediate rows 0..I/G-1, a partial y)."""
+    import torch
+
+    import fp4_routed_expert_amd as moe
+    import synth
+    from fp4_routed_expert_amd import shard
+
+    kind, G = args.shard.split(":")
+    G = int(G)
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(args.config)
+    sh = inp.shape
+    T, H, I, E, k = sh.T, sh.H, sh.I, sh.E, sh.k
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    w = [t(getattr(inp, n)) for n in ("w1", "s1", "w3", "s3", "w2", "s2")]
+    x = t(inp.x.view(np.int16)).view(torch.bfloat16)
+    logits = t(inp.logits)
+    if kind == "ep":
+        Eg = E // G
+        cw = shard.ep_weights(*w, 0, Eg)
+        Ig = I
+    elif kind == "tp":
+        Eg, Ig = E, I // G
+        cw = shard.tp_slice(*w, 0, Ig)
+    else:
+        raise SystemExit(f"--shard {args.shard}: expected ep:G or tp:G")
+    del w
+    nbytes = moe.packed_weight_bytes(Eg, H, Ig)
+    copies = args.copies or max(1, min(8, int(np.ceil(2.0e9 / nbytes))))
+    pws = [moe.prepack_weights(*cw) for _ in range(copies)]
+    del cw
+    P = T * k
+    ids, gates = moe.route_topk(logits, k)
+    counts, offsets, sp, pp = moe.sort_permute(ids, E)
+    xq, xs = moe.quant_act_mxfp8(x)
+    if kind == "ep":
+        o_g, sp_g, (r0, r1) = shard.ep_segment(offsets, sp, 0, Eg)
+        used = int((counts[:Eg] > 0).sum())
+        rows = r1 - r0
+        hq = torch.empty((P, Ig), dtype=torch.uint8, device=dev)
+        hs = torch.empty((P, Ig // 32), dtype=torch.uint8, device=dev)
+        O = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
+        sws = torch.empty(max(moe.stage_workspace_size(T, k, Eg, H, Ig), 256), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            pw = pws[i % copies]
+            moe.expert_up(pw, xq, xs, o_g, sp_g, T, k, args.flags, hq=hq, hs=hs, workspace=sws)
+            moe.expert_down(pw, hq, hs, o_g, T, k, args.flags, O=O, workspace=sws)
+    else:
+        used = int((counts > 0).sum())
+        rows = P
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        lws = torch.empty(max(moe.layer_workspace_size(T, k, Eg, H, Ig, args.flags), 256), dtype=torch.uint8,
+                          device=dev)
+
+        def step(i):
+            moe.layer_forward(pws[i % copies], x, logits, k, args.flags, y=y, workspace=lws)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt / args.steps * 1e3
+    b_w = used * weight_bytes_per_expert(H, Ig, 3)
+    flops = 6.0 * H * Ig * rows
+    name = synth.CONFIG_NAMES.get(args.config, args.config)
+    what = (f"EP shard 1/{G} (experts 0..{Eg - 1}: gate/up + down over their {rows} pairs)" if kind == "ep"
+            else f"TP shard 1/{G} (intermediate rows 0..{Ig - 1}: the whole layer, a partial y)")
+    line = {
+        "metric": METRIC, "value": T * args.steps / dt, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4e2m1xfp8e4m3->fp32", "data": "synthetic",
+        "config": {"workload": f"{name}, {what}", "T": T, "H": H, "I_shard": Ig, "E_shard": Eg, "k": k,
+                   "used_experts": used, "pairs": rows, "weight_copies": copies, "path_flags": args.flags},
+        "shard_weight_tbps": b_w / (ms * 1e-3) / 1e12,
+        "shard_hbm_frac": b_w / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "shard_mfma_frac_fp8": flops / (ms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +418,9 @@ def main():
                     help="step = router GEMM + layer + shared expert (moe_fp4_layer_forward_full)")
     ap.add_argument("--n-shared", type=int, default=1,
                     help="shared experts with --full (packed after the routed ones, same I)")
+    ap.add_argument("--shard", default="",
+                    help="ep:G or tp:G -- time one GPU's share of the layer (experts 0..E/G-1, or "
+                         "the intermediate rows 0..I/G-1); the exchanges between GPUs are not run")
     ap.add_argument("--kernel", default="up_decode_kernel")
     ap.add_argument("--workload", default="")
     args = ap.parse_args()
@@ -350,6 +441,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer's multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
         sys.exit(2)
+    if args.shard:
+        bench_shard(args)
+        return
 
     import torch
 

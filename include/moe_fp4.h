@@ -162,6 +162,10 @@ moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1,
  *   xq [T, H], xs [T, H/32] from moe_quant_act_mxfp8
  *   expert_offsets [E+1], sorted_pair [T*k] from moe_sort_permute
  *   hq [T*k, I] (out), hs [T*k, I/32] (out), rows in sorted order
+ *   An expert-parallel shard may pass expert_offsets[E] < T*k (the pairs of
+ *   its own E experts, offsets re-based to 0): rows from expert_offsets[E]
+ *   on are neither computed nor written, but sorted_pair keeps T*k entries,
+ *   each a valid pair index.  The same holds for moe_fp4_expert_down.
  *   The prefill path needs T*H < 2^32 (MOE_ERR_UNSUPPORTED otherwise).
  *   workspace >= moe_fp4_stage_workspace_size(T, k, E, H, I), 256-aligned
  *   (the prefill path's tile list and its activation scales rearranged by
