@@ -29,10 +29,10 @@
 #define DEC_UP_PIPE 0
 #endif
 #ifndef DEC_DN_NW
-#define DEC_DN_NW 4
+#define DEC_DN_NW 2
 #endif
 #ifndef DEC_DN_B
-#define DEC_DN_B 4
+#define DEC_DN_B 6
 #endif
 #ifndef DEC_DN_PIPE
 #define DEC_DN_PIPE 0
