@@ -169,6 +169,7 @@ def test_router_and_shared_argument_errors():
     assert se(ctypes.byref(d1), A, A, 16, A, MIS, sws, 0, NUL) == INV
     assert se(ctypes.byref(d1), A, A, 16, NUL, A, sws, 0, NUL) == INV
     assert se(ctypes.byref(d1), A, A, 16, A, A, sws, 3, NUL) == INV           # both paths forced
+    assert se(ctypes.byref(d1), NUL, NUL, 0, NUL, NUL, 0, 0, NUL) == 0      # T = 0: no-op
     cs = L.moe_combine_shared
     assert cs(A, A, A, NUL, 4, 2, 256, A, NUL) == INV                        # no shared output
     assert cs(A, A, A, A, 4, 2, 250, A, NUL) == UNS                          # H % 4

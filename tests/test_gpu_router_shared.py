@@ -66,6 +66,8 @@ ROUTER_SHAPES = [
     (16, 7168, 256),     # decode, wide [16]
     (1000, 1024, 96),    # [4]
     (4096, 256, 1024),   # enough output tiles: no K split [1]
+    (20, 256, 1024),     # the largest expert count, medium T [2]
+    (300, 128, 1000),    # tiled, ragged experts, two 64-K stages, no split [1]
 ]
 
 
