@@ -164,6 +164,67 @@ def traffic_summary(fetch_dir: str, write_dir: str, kernel: str, workload: str, 
     return "\n".join(lines)
 
 
+# MI355X: 8 XCDs (GRBM_GUI_ACTIVE sums one count per XCD), 256 CUs x 4 SIMDs.
+N_XCD, N_SIMD = 8, 1024
+MFMA_KERNELS = {  # kernel -> flops per launch as a function of the layer shape (P = T * k)
+    "prefill_gemm_kernel<true>": lambda sh: 4.0 * sh.H * sh.I * sh.T * sh.k,
+    "prefill_gemm_kernel<false>": lambda sh: 2.0 * sh.H * sh.I * sh.T * sh.k,
+}
+
+
+def mfma_summary(pmc_dir: str, workload: str, cfg: str, steps: int) -> str:
+    """Clock and MFMA activity of the prefill GEMMs from one counter run
+    (GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES, SQ_VALU_MFMA_BUSY_CYCLES): the SCLK the
+    kernel ran at (active cycles per XCD over its duration), the share of SIMD
+    cycles with the MFMA pipe busy, and the flop rate against the 5.0 PF FP8
+    peak (at 2.4 GHz) and against that peak scaled to the measured clock."""
+    import csv
+    import glob
+    import synth
+    sh = synth.CONFIGS[cfg]
+    per = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+            name = name.replace("void ", "")
+            d = per.setdefault(name, {}).setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    lines = [
+        f"# MFMA activity and clock: prefill GEMMs, {workload}",
+        "",
+        "Commands (repo root, one MI355X; one counter run):",
+        "",
+        "```",
+        f"rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES --output-format csv "
+        f"-d {pmc_dir} -o m -- python3 bench.py --config {cfg} --steps {steps} --warmup 2 --cpu-budget 0",
+        f"python3 bench.py --mfma-summary {pmc_dir} --workload '{workload}' --config {cfg} --steps {steps}",
+        "```",
+        "",
+        f"SCLK = GRBM_GUI_ACTIVE / {N_XCD} XCDs / kernel duration; MFMA busy = "
+        f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCD} x {N_SIMD} SIMDs); flop rate = the "
+        "algorithmic flops of one launch over its duration (durations are those of the counter run, "
+        "where kernels run serialised).",
+        "",
+        "| kernel | dispatches | duration us | SCLK GHz | MFMA busy | PFLOP/s | of 5.0 PF | of the peak at that SCLK |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for kern, flops in MFMA_KERNELS.items():
+        ds = [d for d in per.get(kern, {}).values()
+              if all(c in d for c in ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES"))]
+        if not ds:
+            raise SystemExit(f"no dispatches of {kern} with the counters in {pmc_dir}: have {sorted(per)}")
+        ns = float(np.mean([d["ns"] for d in ds]))
+        cyc = float(np.mean([d["GRBM_GUI_ACTIVE"] for d in ds])) / N_XCD
+        busy = float(np.mean([d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds])) / (cyc * N_SIMD)
+        ghz = cyc / ns
+        pf = flops(sh) / (ns * 1e-9) / 1e15
+        lines.append(f"| {kern} | {len(ds)} | {ns / 1e3:.1f} | {ghz:.2f} | {100 * busy:.1f} % | {pf:.2f} | "
+                     f"{100 * pf / 5.0:.1f} % | {100 * pf / (5.0 * ghz / 2.4):.1f} % |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 def load_traffic(kernel: str, workload: str):
     """traffic_bytes_per_launch from the committed summary, if it was taken on
     the kernel source as it is now (else None)."""
@@ -414,6 +475,8 @@ def main():
                     help="print a markdown summary of rocprofv3 CSV outputs and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the HBM traffic summary of --kernel from two counter runs and exit")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="print the clock / MFMA-busy summary of the prefill GEMMs from a counter run and exit")
     ap.add_argument("--full", action="store_true",
                     help="step = router GEMM + layer + shared expert (moe_fp4_layer_forward_full)")
     ap.add_argument("--n-shared", type=int, default=1,
@@ -426,6 +489,9 @@ def main():
     args = ap.parse_args()
     if args.rocprof_summary:
         print(rocprof_summary(args.rocprof_summary))
+        return
+    if args.mfma_summary:
+        print(mfma_summary(args.mfma_summary, args.workload, args.config, args.steps))
         return
     if args.traffic_summary:
         print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.kernel, args.workload,
