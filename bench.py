@@ -625,6 +625,14 @@ def main():
         staged_step(args.warmup + i, i)
     torch.cuda.synchronize()
     up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the spread of single steps: each layer call bracketed by its own events
+    # (a separate loop, outside the timed region)
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(args.warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     counts = sort_out[0].cpu().numpy()
     used = int((counts > 0).sum())
 
@@ -668,6 +676,7 @@ def main():
         "config": {"workload": synth.CONFIG_NAMES.get(args.config, args.config), "T": T, "H": H, "I": I,
                    "E": E, "k": k, "seed": sh.seed, "used_experts": used, "weight_copies": copies,
                    "path_flags": args.flags, "launch": "hip_graph" if args.graph else "eager"},
+        "step_ms_p10_p50_p90": [float(v) for v in np.percentile(step_ms, [10, 50, 90])],
         "layer_hbm_tbps": b_layer / (ms_per_step * 1e-3) / 1e12,
         "layer_hbm_frac": b_layer / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_mfma_frac_fp8": flops / (ms_per_step * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
