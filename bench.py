@@ -336,7 +336,7 @@ def bench_dense(args):
         step(args.warmup + i, i)
     torch.cuda.synchronize()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    decode = args.flags == 1 or (args.flags == 0 and T <= 32)
+    decode = args.flags == 1 or (args.flags == 0 and T <= 96)
     b_alg = N * K * (1 + 1 / 32) + T * K * (1 + 1 / 32) + T * N * 2
     f_alg = 2.0 * T * N * K
     wl = synth.DENSE_NAMES.get(args.config, args.config)
@@ -644,7 +644,7 @@ def main():
     up_gbs = b_up / (up_ms * 1e-3) / 1e9
     flops = 6.0 * H * I * P
     up_flops = 4.0 * H * I * P
-    prefill = args.flags == 2 or (args.flags == 0 and P > 16 * Ew)
+    prefill = args.flags == 2 or (args.flags == 0 and P > 14 * Ew)
     if prefill:
         achieved = up_flops / (up_ms * 1e-3) / 1e12
         kname = "prefill_gemm_kernel<true>"

@@ -147,8 +147,10 @@ moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1,
 
 /* Path selection for the expert GEMMs.  By default the host picks from the
  * host-known T*k and E only (never from device counts): the weight-streaming
- * decode path when T*k <= 16*E, the MFMA-tiled prefill path otherwise.  The
- * flags force one path (both compute the same function). */
+ * decode path when T*k <= 14*E (about 14 rows per expert, where the two paths
+ * measured equal on MI355X at both decode-sized expert shapes), the MFMA-tiled
+ * prefill path otherwise.  The flags force one path (both compute the same
+ * function). */
 #define MOE_FLAG_FORCE_DECODE 1u
 #define MOE_FLAG_FORCE_PREFILL 2u
 
@@ -335,7 +337,8 @@ moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/, i
  *
  * moe_fp8_dense_forward: xq [T, K] (16-byte aligned), xs [T, K/32] (4-byte
  * aligned), y [T, N] bf16 bits (out).  T * K < 2^32.  Path: weight streaming
- * for T <= 32 (MOE_FLAG_FORCE_DECODE for any T), an LDS-tiled GEMM otherwise
+ * for T <= 96 (MOE_FLAG_FORCE_DECODE for any T; the two paths measured equal
+ * near T = 106 at K 16384, N 7168), an LDS-tiled GEMM otherwise
  * (MOE_FLAG_FORCE_PREFILL for any T); both compute the same function.  No
  * workspace; the same inputs give the same bits.
  */
