@@ -201,7 +201,10 @@ struct DenseLayout {
 
 // ------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch(es).
-constexpr int kFrontMaxT = 32;  // token counts taken by the fused front kernel
+// Token counts taken by the fused front kernel: at 24 and 32 tokens the
+// stand-alone routing, sort and quantisation measured faster (one workgroup
+// routes every token in the fused kernel), at 16 and below the two are equal.
+constexpr int kFrontMaxT = 16;
 int route_keys_per_lane(int E);
 // The routing launchers read S logit planes T*E floats apart and sum them in
 // plane order (S = 1: plain logits), route over E experts and append ns shared

@@ -224,7 +224,7 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w /*(host)*/,
  * The whole layer, steps 1-7, in one call: route -> sort/permute -> MXFP8(x)
  * -> expert_up -> expert_down -> combine.  Results are bitwise identical to
  * the chain of the single-stage calls above on the same inputs.  For
- * T <= 32 the three front steps run as one fused launch (routing and sort in
+ * T <= 16 the three front steps run as one fused launch (routing and sort in
  * one workgroup, quantisation in the others); larger T uses the stand-alone
  * kernels.  Every intermediate lives in `workspace`
  * (>= moe_fp4_layer_workspace_size(T, k, E, H, I, flags) bytes, 256-aligned;

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("c1", 0),                                                                   # decode, fused front
     (synth.Shape(T=300, H=512, I=256, E=16, k=4, seed=51), moe.MOE_FLAG_FORCE_PREFILL),  # prefill
-    (synth.Shape(T=40, H=256, I=128, E=8, k=2, seed=52), moe.MOE_FLAG_FORCE_DECODE),    # T > 32: stand-alone front
+    (synth.Shape(T=40, H=256, I=128, E=8, k=2, seed=52), moe.MOE_FLAG_FORCE_DECODE),    # T > 16: stand-alone front
 ]
 
 

@@ -2,7 +2,7 @@
 
 It must give bitwise the same y as the chain of single-stage calls (whose
 integer outputs are checked bit-exactly against the oracle elsewhere), and y
-within the output tolerance of the oracle.  Token counts up to 32 take the
+within the output tolerance of the oracle.  Token counts up to 16 take the
 fused front kernel (routing + sort in one workgroup, MXFP8 in the others);
 larger ones the stand-alone kernels, so the shapes below straddle that limit
 and cover every keys-per-lane variant of the routing (E <= 64, 128, 256, 512,
@@ -24,11 +24,15 @@ SHAPES = [
     "c0",
     "c1",
     synth.Shape(T=1, H=128, I=128, E=1, k=1, seed=31),        # one token, one expert
-    synth.Shape(T=32, H=256, I=128, E=100, k=7, seed=32),     # largest fused T, E in (64, 128]
-    synth.Shape(T=17, H=384, I=256, E=256, k=8, seed=33),     # E in (128, 256]
+    synth.Shape(T=16, H=256, I=128, E=100, k=7, seed=37),     # largest fused T, E in (64, 128]
+    synth.Shape(T=17, H=256, I=128, E=100, k=7, seed=38),     # just past the fused limit
+    synth.Shape(T=32, H=256, I=128, E=100, k=7, seed=32),     # stand-alone front, E in (64, 128]
+    synth.Shape(T=16, H=384, I=256, E=256, k=8, seed=33),     # fused, E in (128, 256]
+    synth.Shape(T=20, H=384, I=256, E=256, k=8, seed=40),     # stand-alone front, E in (128, 256]
     synth.Shape(T=9, H=128, I=128, E=400, k=5, seed=34),      # E in (256, 512]
+    synth.Shape(T=16, H=128, I=128, E=1024, k=32, seed=39),   # fused, E = 1024, k = 32: P = 512
     synth.Shape(T=32, H=128, I=128, E=1024, k=32, seed=35),   # E = 1024, k = 32: P = 1024
-    synth.Shape(T=33, H=256, I=128, E=65, k=7, seed=36),      # just past the fused limit
+    synth.Shape(T=33, H=256, I=128, E=65, k=7, seed=36),      # stand-alone front, E = 65
 ]
 
 
