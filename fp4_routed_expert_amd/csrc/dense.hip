@@ -372,13 +372,45 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
     }
 }
 
-// the two geometries: 128 x 128 (4 waves) and, from 256 tokens, 192 x 256 (8 waves;
-// 256 x 256 does not fit 2 waves per SIMD without spills, 192 x 256 is 11 % faster than
-// 128 x 128 on 4604 tokens: fewer bytes staged per flop)
+// The two geometries: 128 x 128 (4 waves) and 192 x 256 (8 waves; 256 x 256 does
+// not fit 2 waves per SIMD without spills).  The large tile stages fewer bytes
+// per flop (11 % faster on 4604 tokens) but a workgroup of either runs its
+// whole K range, so below a few thousand tokens the time is set by how many
+// rounds of workgroups the CUs take: two small workgroups share a CU, one
+// large one fills it, and a round of large tiles measured 1.16x a round of
+// small ones (K 16384, N 7168; T from 97 to 4604).
 constexpr int kLWM = 2, kLWN = 4, kLSM = 6, kLSets = 2;
 using DSmall = DCfg<2, 2, 4>;
 using DLarge = DCfg<kLWM, kLWN, kLSM>;
-constexpr int kDenseLargeMinT = 256;
+
+// Resident workgroups per CU of each geometry and the CU count, once per device.
+struct DenseOccupancy {
+  int ncu = 0, small = 0, large = 0;
+};
+
+DenseOccupancy dense_occupancy() {
+  static DenseOccupancy cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  DenseOccupancy& o = cached[dev];
+  if (o.ncu == 0) {
+    DenseOccupancy n;
+    if (hipDeviceGetAttribute(&n.ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n.ncu < 1)
+      n.ncu = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n.small, reinterpret_cast<const void*>(&dense_prefill_kernel<2, 2, 4, 2>), DSmall::NT,
+            0) != hipSuccess || n.small < 1)
+      n.small = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n.large,
+            reinterpret_cast<const void*>(&dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets>),
+            DLarge::NT, 0) != hipSuccess || n.large < 1)
+      n.large = 1;
+    o = n;
+  }
+  return o;
+}
 
 }  // namespace
 
@@ -402,7 +434,15 @@ hipError_t launch_dense_decode(const uint8_t* packed, const uint8_t* xq, const u
 
 hipError_t launch_dense_prefill(const uint8_t* packed, const uint8_t* xq, const uint8_t* xs, int T,
                                 int N, int K, uint16_t* y, hipStream_t s) {
-  if (T >= kDenseLargeMinT) {
+  const DenseOccupancy occ = dense_occupancy();
+  const long wg_small = (long)((T + DSmall::BM - 1) / DSmall::BM) *
+                        ((N + 16 * DSmall::BT - 1) / (16 * DSmall::BT));
+  const long wg_large = (long)((T + DLarge::BM - 1) / DLarge::BM) *
+                        ((N + 16 * DLarge::BT - 1) / (16 * DLarge::BT));
+  const long slots_small = (long)occ.small * occ.ncu, slots_large = (long)occ.large * occ.ncu;
+  const long rounds_small = (wg_small + slots_small - 1) / slots_small;
+  const long rounds_large = (wg_large + slots_large - 1) / slots_large;
+  if (116 * rounds_large < 100 * rounds_small) {
     const long blocks = (long)((T + DLarge::BM - 1) / DLarge::BM) *
                         ((N + 16 * DLarge::BT - 1) / (16 * DLarge::BT));
     hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets>), dim3((unsigned)blocks),

@@ -2,7 +2,8 @@
 
 y (bf16) against the oracle's fp64 sums on the same MXFP8 rows, on both
 paths (weight streaming and the LDS-tiled GEMM, in both of its tile
-geometries): the tiny workload, ragged
+geometries, the larger one taken when the smaller would need more rounds of
+workgroups): the tiny workload, ragged
 token counts, an odd K-step count (the tiled kernel's zero padding step),
 weight-row counts that leave a partial 128-row tile, the decode-shaped and
 prefill-shaped projections at full size (sampled tokens), plus the prepacked
@@ -52,7 +53,7 @@ SMALL = [
     ("d0", dict(T=37, K=384, N=160)),             # odd K-step count, partial row tile
     ("d0", dict(T=130, K=256, N=288)),            # two token tiles (ragged), three row tiles
     ("d0", dict(T=1, K=128, N=32)),               # smallest
-    ("d0", dict(T=300, K=384, N=288)),            # large-tile geometry: ragged tokens and rows, odd K-steps
+    ("d0", dict(T=300, K=384, N=288)),            # ragged tokens and rows, odd K-steps
 ]
 
 
@@ -84,6 +85,22 @@ def test_dense_full_size(cfg, ntok, dev):
     y2 = moe.dense_layer(c.dw, c.x)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_dense_large_tile_geometry(dev):
+    """1300 tokens x 7136 rows: the 128 x 128 tiles would need two rounds of
+    workgroups on 256 CUs and the 192 x 256 tiles one, so the larger geometry
+    runs -- ragged in tokens (1300 = 6 x 192 + 148) and rows (7136 = 27 x 256 +
+    224), with an odd K-step count; sampled tokens plus the ragged tail."""
+    c = get_dense("d0", dev, T=1300, K=384, N=7136)
+    log("[dense] large-tile geometry T1300 K384 N7136")
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    y = moe.dense_forward(c.dw, xq, xs, PRE)
+    y_auto = moe.dense_forward(c.dw, xq, xs)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_auto.view(torch.int16))
+    toks = np.unique(np.concatenate([sample_tokens(c.sh.T, 40, seed=5), np.arange(1290, 1300)])).astype(np.int32)
+    check_y(y.float().cpu().numpy()[toks], c.ref(toks), "dense/large-geometry")
 
 
 def _unpack(packed: np.ndarray, N: int, K: int):
