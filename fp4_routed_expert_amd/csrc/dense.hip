@@ -268,14 +268,25 @@ __device__ __forceinline__ void dense_compute(v4f (&acc)[kSM][4], const uint8_t*
   }
 }
 
-template <int kWM, int kWN, int kSM, int kSets>
-__global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
+// kSplit groups of kWM x kWN waves split the K-steps of one tile: group g
+// runs the whole pipeline below on its own share with its own two LDS
+// stages, and the groups' partial sums are added in group order at the end
+// (for tiles too few to give every CU one).
+template <int kWM, int kWN, int kSM, int kSets, int kSplit>
+__global__ __launch_bounds__(64 * kWM * kWN * kSplit) void dense_prefill_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xs, int T, int N, int K, uint16_t* __restrict__ y) {
   using C = DCfg<kWM, kWN, kSM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
+  static_assert(kSplit == 1 || kSplit == 2, "one or two K groups");
+  static_assert(kSplit == 1 || kWM * kWN * kSM * 4 * 64 * 16 <= 2 * C::STAGE,
+                "a group's partial sums fit its two stages");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kSplit * 2 * C::STAGE];
   const DenseLayout L(N, K);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (compile-time zero / identity without a split: the unsplit kernel keeps
+  // its register count, and with it two workgroups per CU)
+  const int grp = kSplit == 1 ? 0 : (int)threadIdx.x / C::NT;                 // K group
+  const int tid = kSplit == 1 ? (int)threadIdx.x : (int)threadIdx.x % C::NT;  // thread in the group
+  const int lane = tid & 63, wave = tid >> 6;   // wave within the group
   const int wm = wave / kWN, wn = wave % kWN;
   const int NTn = (N + 16 * C::BT - 1) / (16 * C::BT);
   // weight-row tiles vary fastest: the token tile's x rows stay in L2 while its
@@ -283,7 +294,11 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
   const int bn = (int)(blockIdx.x % (unsigned)NTn), bm = (int)(blockIdx.x / (unsigned)NTn);
   const int m0 = bm * C::BM, nt0 = bn * C::BT;  // first token, first 16-row weight tile
   const int ntiles = N / 16;
-  const int J = L.J;
+  // this group's K-steps [j0, J) (J re-based as its end); steps past it load
+  // zeros, like the padding step of an odd count
+  const int Jg = kSplit == 1 ? L.J : (L.J + kSplit - 1) / kSplit;
+  const int j0 = kSplit == 1 ? 0 : grp * Jg;
+  const int J = kSplit == 1 ? L.J : min(L.J, j0 + Jg);
 
   DSrc<C> src;
 #pragma unroll
@@ -318,16 +333,18 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
   // run in pairs; an odd count gets a zero padding step (a step left over
   // after the loop would make the compiler rename the accumulators, doubling
   // their registers).
-  const int J2 = J + (J & 1);
-  uint8_t* const buf0 = lds;
-  uint8_t* const buf1 = lds + C::STAGE;
+  // every group takes the same number of loop trips (the barriers are the
+  // workgroup's): Jg rounded up to even
+  const int J2 = Jg + (Jg & 1);
+  uint8_t* const buf0 = kSplit == 1 ? lds : lds + grp * 2 * C::STAGE;
+  uint8_t* const buf1 = buf0 + C::STAGE;
   if constexpr (kSets == 2) {
     DLoad<C> p, q;
-    dense_gload<C>(p, xq, packed, src, 0, J);
-    dense_gload<C>(q, xq, packed, src, 1, J);
-    dense_lstore<C>(p, lds, tid);
+    dense_gload<C>(p, xq, packed, src, j0, J);
+    dense_gload<C>(q, xq, packed, src, j0 + 1, J);
+    dense_lstore<C>(p, buf0, tid);
     __syncthreads();
-    for (int j = 0; j < J2; j += 2) {
+    for (int j = j0; j < j0 + J2; j += 2) {
       dense_gload<C>(p, xq, packed, src, j + 2, J);
       dense_compute<C, kSM>(acc, buf0, wm, wn, lane);
       dense_lstore<C>(q, buf1, tid);
@@ -339,10 +356,10 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
     }
   } else {
     DLoad<C> p;
-    dense_gload<C>(p, xq, packed, src, 0, J);
-    dense_lstore<C>(p, lds, tid);
+    dense_gload<C>(p, xq, packed, src, j0, J);
+    dense_lstore<C>(p, buf0, tid);
     __syncthreads();
-    for (int j = 0; j < J2; j += 2) {
+    for (int j = j0; j < j0 + J2; j += 2) {
       dense_gload<C>(p, xq, packed, src, j + 1, J);
       dense_compute<C, kSM>(acc, buf0, wm, wn, lane);
       dense_lstore<C>(p, buf1, tid);
@@ -352,6 +369,22 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_prefill_kernel(
       dense_lstore<C>(p, buf0, tid);
       __syncthreads();
     }
+  }
+  if constexpr (kSplit == 2) {
+    // group 1 parks its sums in its own (now idle) stages, group 0 adds them
+    v4f* part = reinterpret_cast<v4f*>(lds + 2 * C::STAGE) + (wave * kSM * 4) * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < kSM; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) part[(i * 4 + t) * 64] = acc[i][t];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int i = 0; i < kSM; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[i][t] += part[(i * 4 + t) * 64];
   }
 
   // the wave's 4 tiles are 64 consecutive outputs of a token row: its 128
@@ -399,12 +432,12 @@ DenseOccupancy dense_occupancy() {
         n.ncu < 1)
       n.ncu = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n.small, reinterpret_cast<const void*>(&dense_prefill_kernel<2, 2, 4, 2>), DSmall::NT,
+            &n.small, reinterpret_cast<const void*>(&dense_prefill_kernel<2, 2, 4, 2, 1>), DSmall::NT,
             0) != hipSuccess || n.small < 1)
       n.small = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n.large,
-            reinterpret_cast<const void*>(&dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets>),
+            reinterpret_cast<const void*>(&dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets, 1>),
             DLarge::NT, 0) != hipSuccess || n.large < 1)
       n.large = 1;
     o = n;
@@ -445,14 +478,16 @@ hipError_t launch_dense_prefill(const uint8_t* packed, const uint8_t* xq, const 
   if (116 * rounds_large < 100 * rounds_small) {
     const long blocks = (long)((T + DLarge::BM - 1) / DLarge::BM) *
                         ((N + 16 * DLarge::BT - 1) / (16 * DLarge::BT));
-    hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets, 1>), dim3((unsigned)blocks),
                        dim3(DLarge::NT), 0, s,
                        packed, xq, xs, T, N, K, y);
+  } else if (wg_small <= occ.ncu) {
+    // fewer small tiles than CUs: each tile's K-steps split over two wave groups
+    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2, 2>), dim3((unsigned)wg_small),
+                       dim3(2 * DSmall::NT), 0, s, packed, xq, xs, T, N, K, y);
   } else {
-    const long blocks = (long)((T + DSmall::BM - 1) / DSmall::BM) *
-                        ((N + 16 * DSmall::BT - 1) / (16 * DSmall::BT));
-    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2>), dim3((unsigned)blocks), dim3(DSmall::NT), 0, s,
-                       packed, xq, xs, T, N, K, y);
+    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2, 1>), dim3((unsigned)wg_small),
+                       dim3(DSmall::NT), 0, s, packed, xq, xs, T, N, K, y);
   }
   return hipGetLastError();
 }

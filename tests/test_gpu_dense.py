@@ -3,7 +3,8 @@
 y (bf16) against the oracle's fp64 sums on the same MXFP8 rows, on both
 paths (weight streaming and the LDS-tiled GEMM, in both of its tile
 geometries, the larger one taken when the smaller would need more rounds of
-workgroups): the tiny workload, ragged
+workgroups, and the smaller one's K range split over two wave groups when
+its tiles are fewer than the CUs): the tiny workload, ragged
 token counts, an odd K-step count (the tiled kernel's zero padding step),
 weight-row counts that leave a partial 128-row tile, the decode-shaped and
 prefill-shaped projections at full size (sampled tokens), plus the prepacked
@@ -53,7 +54,7 @@ SMALL = [
     ("d0", dict(T=37, K=384, N=160)),             # odd K-step count, partial row tile
     ("d0", dict(T=130, K=256, N=288)),            # two token tiles (ragged), three row tiles
     ("d0", dict(T=1, K=128, N=32)),               # smallest
-    ("d0", dict(T=300, K=384, N=288)),            # ragged tokens and rows, odd K-steps
+    ("d0", dict(T=300, K=384, N=288)),            # ragged tokens and rows, odd K-steps (two K groups)
 ]
 
 
@@ -101,6 +102,19 @@ def test_dense_large_tile_geometry(dev):
     assert torch.equal(y.view(torch.int16), y_auto.view(torch.int16))
     toks = np.unique(np.concatenate([sample_tokens(c.sh.T, 40, seed=5), np.arange(1290, 1300)])).astype(np.int32)
     check_y(y.float().cpu().numpy()[toks], c.ref(toks), "dense/large-geometry")
+
+
+def test_dense_small_tile_unsplit(dev):
+    """1100 tokens x 4096 rows: 288 small tiles, more than the CUs, so each
+    runs its whole K range (two share a CU) -- the unsplit small geometry,
+    ragged tokens, odd K-step count; the tiles below take two K groups."""
+    c = get_dense("d0", dev, T=1100, K=384, N=4096)
+    log("[dense] small tile, unsplit: T1100 K384 N4096")
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    y = moe.dense_forward(c.dw, xq, xs, PRE)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([sample_tokens(c.sh.T, 40, seed=6), np.arange(1090, 1100)])).astype(np.int32)
+    check_y(y.float().cpu().numpy()[toks], c.ref(toks), "dense/small-unsplit")
 
 
 def _unpack(packed: np.ndarray, N: int, K: int):
