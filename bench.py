@@ -90,7 +90,7 @@ def rocprof_summary(paths) -> str:
 
 
 KERNEL_SOURCES = {
-    "up_decode_kernel": "fp4_routed_expert_amd/csrc/expert_decode.hip",
+    "up_decode_kernel<1>": "fp4_routed_expert_amd/csrc/expert_decode.hip",
     "prefill_gemm_kernel<true>": "fp4_routed_expert_amd/csrc/expert_prefill.hip",
     DENSE_DECODE_KERNEL: "fp4_routed_expert_amd/csrc/dense.hip",
     DENSE_PREFILL_KERNEL: "fp4_routed_expert_amd/csrc/dense.hip",
@@ -484,7 +484,7 @@ def main():
     ap.add_argument("--shard", default="",
                     help="ep:G or tp:G -- time one GPU's share of the layer (experts 0..E/G-1, or "
                          "the intermediate rows 0..I/G-1); the exchanges between GPUs are not run")
-    ap.add_argument("--kernel", default="up_decode_kernel")
+    ap.add_argument("--kernel", default="up_decode_kernel<1>")
     ap.add_argument("--workload", default="")
     args = ap.parse_args()
     if args.rocprof_summary:
@@ -644,7 +644,7 @@ def main():
     up_gbs = b_up / (up_ms * 1e-3) / 1e9
     flops = 6.0 * H * I * P
     up_flops = 4.0 * H * I * P
-    prefill = args.flags == 2 or (args.flags == 0 and P > 14 * Ew)
+    prefill = args.flags == 2 or (args.flags == 0 and P > 16 * Ew)
     if prefill:
         achieved = up_flops / (up_ms * 1e-3) / 1e12
         kname = "prefill_gemm_kernel<true>"
@@ -654,7 +654,7 @@ def main():
                 "traffic": load_traffic(kname, synth.CONFIG_NAMES.get(args.config, args.config)),
                 "alg_flops_per_launch": up_flops, "avg_launch_us": up_ms * 1e3}
     else:
-        kname = "up_decode_kernel"
+        kname = "up_decode_kernel<1>"
         roof = {"bound": "hbm", "kernel": kname + " (gate/up GEMM + SwiGLU + MXFP8 of h)",
                 "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": up_gbs / HBM_PEAK_GBS,

@@ -224,13 +224,15 @@ hipError_t launch_quant_mxfp8(const uint16_t* x, long M, int K, uint8_t* q, uint
 hipError_t launch_prepack(const uint8_t* w1, const uint8_t* s1, const uint8_t* w3,
                           const uint8_t* s3, const uint8_t* w2, const uint8_t* s2,
                           const PackedLayout& L, uint8_t* packed, hipStream_t s);
+// row_groups (1 or 2): 16-row groups of an expert's pairs per pass over its
+// weights.
 hipError_t launch_up_decode(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
                             const uint8_t* xs, const int32_t* offsets,
                             const int32_t* sorted_pair, int k, uint8_t* hq, uint8_t* hs,
-                            hipStream_t s);
+                            int row_groups, hipStream_t s);
 hipError_t launch_down_decode(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
                               const uint8_t* hs, const int32_t* offsets, uint16_t* O,
-                              hipStream_t s);
+                              int row_groups, hipStream_t s);
 size_t prefill_stage_bytes(long P, int E, int H, int I);
 hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
                              const uint8_t* xs, const int32_t* offsets,

@@ -147,8 +147,8 @@ moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1,
 
 /* Path selection for the expert GEMMs.  By default the host picks from the
  * host-known T*k and E only (never from device counts): the weight-streaming
- * decode path when T*k <= 14*E (about 14 rows per expert, where the two paths
- * measured equal on MI355X at both decode-sized expert shapes), the MFMA-tiled
+ * decode path when T*k <= 16*E (about 16 rows per expert, where the two paths
+ * measured equal on MI355X at the larger decode-sized expert shape), the MFMA-tiled
  * prefill path otherwise.  The flags force one path (both compute the same
  * function). */
 #define MOE_FLAG_FORCE_DECODE 1u

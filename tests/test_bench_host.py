@@ -33,7 +33,7 @@ def _row(disp, kernel, counter, value, t0=0, t1=1000):
 
 def test_traffic_summary_scales_by_the_copy(tmp_path):
     gib_kib = 1 << 20
-    kern = "up_decode_kernel"
+    kern = "up_decode_kernel<1>"
     full = f"moe::(anonymous namespace)::{kern}(unsigned char const*, int)"
     copy = "__amd_rocclr_copyBuffer"
     # the copy of 1 GiB reads as half a GiB of FETCH_SIZE and a whole GiB of WRITE_SIZE
@@ -53,7 +53,7 @@ def test_traffic_summary_names_missing_kernels(tmp_path):
     _write_counters(tmp_path / "f", [_row(0, "other_kernel(int)", "FETCH_SIZE", 1.0)])
     _write_counters(tmp_path / "w", [_row(0, "other_kernel(int)", "WRITE_SIZE", 1.0)])
     with pytest.raises(SystemExit, match="missing kernels"):
-        bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), "up_decode_kernel", "wl")
+        bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), "up_decode_kernel<1>", "wl")
 
 
 def test_mfma_summary_clock_busy_and_rate(tmp_path):
@@ -84,7 +84,7 @@ def test_mfma_summary_clock_busy_and_rate(tmp_path):
 
 
 def test_traffic_figure_needs_the_current_source(tmp_path, monkeypatch):
-    kern = "up_decode_kernel"
+    kern = "up_decode_kernel<1>"
     src = tmp_path / "kernel.hip"
     src.write_text("// version 1\n")
     (tmp_path / "profiles").mkdir()
