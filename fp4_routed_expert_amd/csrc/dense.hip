@@ -23,6 +23,8 @@
 // in flight; partial sums meet in LDS in wave order.  Prefill: LDS-tiled
 // GEMM, 128 tokens x 128 rows per workgroup, 128 K per stage, two register
 // sets so that one stage loads while another multiplies.
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -421,12 +423,21 @@ struct DenseOccupancy {
   int ncu = 0, small = 0, large = 0;
 };
 
+// (Packed in one atomic word per device: concurrent first calls from several
+// host threads store the same value.)
 DenseOccupancy dense_occupancy() {
-  static DenseOccupancy cached[64];
+  static std::atomic<uint64_t> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  DenseOccupancy& o = cached[dev];
-  if (o.ncu == 0) {
+  const uint64_t w = cached[dev].load(std::memory_order_relaxed);
+  if (w != 0) {
+    DenseOccupancy o;
+    o.ncu = (int)(w & 0xFFFFFu);
+    o.small = (int)((w >> 20) & 0xFFFFFu);
+    o.large = (int)(w >> 40);
+    return o;
+  }
+  {
     DenseOccupancy n;
     if (hipDeviceGetAttribute(&n.ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n.ncu < 1)
@@ -440,9 +451,11 @@ DenseOccupancy dense_occupancy() {
             reinterpret_cast<const void*>(&dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets, 1>),
             DLarge::NT, 0) != hipSuccess || n.large < 1)
       n.large = 1;
-    o = n;
+    cached[dev].store((uint64_t)(n.ncu & 0xFFFFF) | ((uint64_t)(n.small & 0xFFFFF) << 20) |
+                          ((uint64_t)n.large << 40),
+                      std::memory_order_relaxed);
+    return n;
   }
-  return o;
 }
 
 }  // namespace

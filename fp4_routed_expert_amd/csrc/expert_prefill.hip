@@ -55,6 +55,8 @@
 // SwiGLU stays in its registers.  The number of live sub-tiles is a
 // compile-time parameter of the loop body, selected once per wave, so the
 // MFMA stream has no conditionals and only live accumulators are allocated.
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -699,17 +701,20 @@ size_t tile_list_bytes(long P, int E) { return align256_(kTileHdr + (size_t)max_
 
 // One workgroup per compute unit (the kernel's LDS allows no more), rounded
 // down to whole rounds of the 8 XCDs; queried once per device.
+// (Atomic: concurrent first calls from several host threads store the same value.)
 unsigned persistent_grid() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int ncu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
       ncu = 256;
-    cached[dev] = ncu / 8 * 8;
+    v = ncu / 8 * 8;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return (unsigned)cached[dev];
+  return (unsigned)v;
 }
 
 }  // namespace
