@@ -40,7 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true>"   # the instantiations the library launches
+DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true, 1>"   # the instantiations the library launches
 DENSE_PREFILL_KERNEL = "dense_prefill_kernel<2, 4, 6, 2, 1>"  # (prefill: the 192 x 256 tile)
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 (and FP8 x FP4 scaled MFMA at the FP8 issue rate)
 METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU"
@@ -336,7 +336,7 @@ def bench_dense(args):
         step(args.warmup + i, i)
     torch.cuda.synchronize()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    decode = args.flags == 1 or (args.flags == 0 and T <= 80)
+    decode = args.flags == 1 or (args.flags == 0 and T <= 96)
     b_alg = N * K * (1 + 1 / 32) + T * K * (1 + 1 / 32) + T * N * 2
     f_alg = 2.0 * T * N * K
     wl = synth.DENSE_NAMES.get(args.config, args.config)

@@ -64,18 +64,19 @@ __global__ __launch_bounds__(256) void dense_pack_kernel(const uint8_t* __restri
 // ------------------------------------------------------------------ decode
 // One K-step of a wave: NT weight tiles and their scale bytes, the activation
 // fragment (token row r, the same two 16-byte pieces) and its scale byte.
-template <int NT>
+// NG token tiles of 16 share each loaded weight tile (NG MFMAs per tile).
+template <int NT, int NG = 1>
 struct DStep {
-  v4u b0[NT], b1[NT], a0, a1;
-  uint32_t sb[NT], sa;
+  v4u b0[NT], b1[NT], a0[NG], a1[NG];
+  uint32_t sb[NT], sa[NG];
 };
 
 // wt[t]/st[t]: this lane's bytes of tile (nt0 + t, 0) and its scale; K-step j
 // is kTileStep * j further (scales: kScaleStep * j).
-template <int NT>
-__device__ __forceinline__ void dload(DStep<NT>& s, const uint8_t* const (&wt)[NT],
-                                      const uint8_t* const (&st)[NT], const uint8_t* arow,
-                                      const uint8_t* as, int j) {
+template <int NT, int NG>
+__device__ __forceinline__ void dload(DStep<NT, NG>& s, const uint8_t* const (&wt)[NT],
+                                      const uint8_t* const (&st)[NT], const uint8_t* const (&arow)[NG],
+                                      const uint8_t* const (&as)[NG], int j) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const uint8_t* w = wt[t] + (size_t)j * DenseLayout::kTileStep;
@@ -84,24 +85,32 @@ __device__ __forceinline__ void dload(DStep<NT>& s, const uint8_t* const (&wt)[N
     s.b1[t] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(w + 1024));
     s.sb[t] = st[t][(size_t)j * DenseLayout::kScaleStep];
   }
-  s.a0 = *reinterpret_cast<const v4u*>(arow + (size_t)j * 128);
-  s.a1 = *reinterpret_cast<const v4u*>(arow + (size_t)j * 128 + 64);
-  s.sa = as[(size_t)j * 4];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    s.a0[g] = *reinterpret_cast<const v4u*>(arow[g] + (size_t)j * 128);
+    s.a1[g] = *reinterpret_cast<const v4u*>(arow[g] + (size_t)j * 128 + 64);
+    s.sa[g] = as[g][(size_t)j * 4];
+  }
 }
 
-template <int NT>
-__device__ __forceinline__ void dmma(const DStep<NT>& s, v4f (&acc)[NT]) {
-  const v8i a = cat8(s.a0, s.a1);
+// acc[g * NT + t]: token tile g, weight tile t
+template <int NT, int NG>
+__device__ __forceinline__ void dmma(const DStep<NT, NG>& s, v4f (&acc)[NG * NT]) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    acc[t] = mfma_fp8_fp8(a, cat8(s.b0[t], s.b1[t]), acc[t], (int)s.sa, (int)s.sb[t]);
+  for (int g = 0; g < NG; ++g) {
+    const v8i a = cat8(s.a0[g], s.a1[g]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc[g * NT + t] = mfma_fp8_fp8(a, cat8(s.b0[t], s.b1[t]), acc[g * NT + t], (int)s.sa[g], (int)s.sb[t]);
+  }
 }
 
 // NW waves split the K-steps: with kIlv wave w takes steps w, w + NW, ...
 // (the workgroup's waves read neighbouring tiles at any moment), else one
 // contiguous range each.  NT row tiles per workgroup share each activation
-// fragment.
-template <int NW, int kB, int NT, bool kIlv>
+// fragment, NG token tiles of 16 each weight tile (the workgroup then covers
+// tokens 16 NG mt .. +16 NG).
+template <int NW, int kB, int NT, bool kIlv, int NG>
 __global__ __launch_bounds__(64 * NW) void dense_decode_kernel(const uint8_t* __restrict__ packed,
                                                                const uint8_t* __restrict__ xq,
                                                                const uint8_t* __restrict__ xs,
@@ -125,7 +134,8 @@ __global__ __launch_bounds__(64 * NW) void dense_decode_kernel(const uint8_t* __
     nsteps = ((wave + 1) * J) / NW - js;
   }
   // this lane's pieces: weight tile lane offset (tiles past N clamped to the
-  // last one, never stored), activation row 16 mt + r (clamped the same way)
+  // last one, never stored), activation rows 16 (NG mt + tg) + r (clamped the
+  // same way)
   const uint8_t* wt[NT];
   const uint8_t* st[NT];
 #pragma unroll
@@ -134,46 +144,53 @@ __global__ __launch_bounds__(64 * NW) void dense_decode_kernel(const uint8_t* __
     wt[t] = packed + L.tile_off(ntc, 0) + lane * 16;
     st[t] = packed + L.scale_off(ntc, 0) + lane;
   }
-  const int trow = min(16 * mt + r, T - 1);
-  const uint8_t* arow = xq + (size_t)trow * K + 16 * g;
-  const uint8_t* as = xs + (size_t)trow * (K / 32) + g;
-
-  v4f acc[NT];
+  const uint8_t* arow[NG];
+  const uint8_t* as[NG];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  DStep<NT> s[kB];
+  for (int tg = 0; tg < NG; ++tg) {
+    const int trow = min(16 * (NG * mt + tg) + r, T - 1);
+    arow[tg] = xq + (size_t)trow * K + 16 * g;
+    as[tg] = xs + (size_t)trow * (K / 32) + g;
+  }
+
+  v4f acc[NG * NT];
+#pragma unroll
+  for (int t = 0; t < NG * NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  DStep<NT, NG> s[kB];
   int u = 0;
   // whole batches: kB steps' loads back to back, then their MFMAs
   for (; u + kB <= nsteps; u += kB) {
 #pragma unroll
-    for (int b = 0; b < kB; ++b) dload<NT>(s[b], wt, st, arow, as, js + jstep * (u + b));
+    for (int b = 0; b < kB; ++b) dload<NT, NG>(s[b], wt, st, arow, as, js + jstep * (u + b));
 #pragma unroll
-    for (int b = 0; b < kB; ++b) dmma<NT>(s[b], acc);
+    for (int b = 0; b < kB; ++b) dmma<NT, NG>(s[b], acc);
   }
   for (; u < nsteps; ++u) {
-    dload<NT>(s[0], wt, st, arow, as, js + jstep * u);
-    dmma<NT>(s[0], acc);
+    dload<NT, NG>(s[0], wt, st, arow, as, js + jstep * u);
+    dmma<NT, NG>(s[0], acc);
   }
 
   // fixed-order sum of the waves' partials, then bf16 stores of the valid tokens
-  __shared__ v4f red[NW][NT][64];
+  __shared__ v4f red[NW][NG * NT][64];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
+  for (int t = 0; t < NG * NT; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (nt0 + t >= ntiles) break;
-    v4f a = red[0][t][lane];
+  for (int tg = 0; tg < NG; ++tg)
 #pragma unroll
-    for (int w = 1; w < NW; ++w) a += red[w][t][lane];
-    const int n = 16 * (nt0 + t) + r;  // D column = weight row
+    for (int t = 0; t < NT; ++t) {
+      if (nt0 + t >= ntiles) break;
+      v4f a = red[0][tg * NT + t][lane];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int tk = 16 * mt + 4 * g + v;  // D row = token
-      if (tk < T) y[(size_t)tk * N + n] = f32_to_bf16(a[v]);
+      for (int w = 1; w < NW; ++w) a += red[w][tg * NT + t][lane];
+      const int n = 16 * (nt0 + t) + r;  // D column = weight row
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tk = 16 * (NG * mt + tg) + 4 * g + v;  // D row = token
+        if (tk < T) y[(size_t)tk * N + n] = f32_to_bf16(a[v]);
+      }
     }
-  }
 }
 
 // ----------------------------------------------------------------- prefill
@@ -472,9 +489,16 @@ hipError_t launch_dense_decode(const uint8_t* packed, const uint8_t* xq, const u
                                int N, int K, uint16_t* y, hipStream_t s) {
   constexpr int kNW = 16, kBt = 2, kNT = 2;
   constexpr bool kIl = true;
-  const dim3 grid((unsigned)((N / 16 + kNT - 1) / kNT), (unsigned)((T + 15) / 16));
-  hipLaunchKernelGGL((dense_decode_kernel<kNW, kBt, kNT, kIl>), grid, dim3(64 * kNW), 0, s, packed,
-                     xq, xs, T, N, K, y);
+  // from 17 tokens two token tiles share each pass over the weights
+  if (T > 16) {
+    const dim3 grid((unsigned)((N / 16 + kNT - 1) / kNT), (unsigned)((T + 31) / 32));
+    hipLaunchKernelGGL((dense_decode_kernel<kNW, kBt, kNT, kIl, 2>), grid, dim3(64 * kNW), 0, s,
+                       packed, xq, xs, T, N, K, y);
+  } else {
+    const dim3 grid((unsigned)((N / 16 + kNT - 1) / kNT), (unsigned)((T + 15) / 16));
+    hipLaunchKernelGGL((dense_decode_kernel<kNW, kBt, kNT, kIl, 1>), grid, dim3(64 * kNW), 0, s,
+                       packed, xq, xs, T, N, K, y);
+  }
   return hipGetLastError();
 }
 

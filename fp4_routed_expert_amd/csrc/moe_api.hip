@@ -22,10 +22,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
-// dense projection: weight streaming up to 5 token tiles (streaming measured
-// faster than the tiled GEMM up to T = 80 at K 16384, N 7168: 112 vs 115 us;
-// 128 vs 116 us at T = 88)
-constexpr int kDenseDecodeMaxT = 80;
+// dense projection: weight streaming up to 3 passes of two token tiles
+// (streaming measured faster than the tiled GEMM up to T = 96 at K 16384,
+// N 7168: 99 vs 116 us; 133 vs 119 us at T = 128)
+constexpr int kDenseDecodeMaxT = 96;
 // expert GEMMs: weight streaming while T*k <= this many rows per expert (the
 // measured crossover of the two paths at the decode-sized expert shapes)
 constexpr int64_t kDecodeRowsPerExpert = 16;

@@ -337,8 +337,8 @@ moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/, i
  *
  * moe_fp8_dense_forward: xq [T, K] (16-byte aligned), xs [T, K/32] (4-byte
  * aligned), y [T, N] bf16 bits (out).  T * K < 2^32.  Path: weight streaming
- * for T <= 80 (MOE_FLAG_FORCE_DECODE for any T; the two paths measured equal
- * near T = 82 at K 16384, N 7168), an LDS-tiled GEMM otherwise
+ * for T <= 96 (MOE_FLAG_FORCE_DECODE for any T; the two paths measured equal
+ * near T = 110 at K 16384, N 7168), an LDS-tiled GEMM otherwise
  * (MOE_FLAG_FORCE_PREFILL for any T); both compute the same function.  No
  * workspace; the same inputs give the same bits.
  */

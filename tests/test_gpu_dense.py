@@ -76,7 +76,7 @@ def test_dense_full_size(cfg, ntok, dev):
     c = get_dense(cfg, dev)
     log(f"[dense] {cfg} full size")
     y = moe.dense_layer(c.dw, c.x)
-    y_other = moe.dense_layer(c.dw, c.x, PRE) if c.sh.T <= 80 else None   # the other path
+    y_other = moe.dense_layer(c.dw, c.x, PRE) if c.sh.T <= 96 else None   # the other path
     torch.cuda.synchronize()
     toks = sample_tokens(c.sh.T, ntok, seed=13)
     ref = c.ref(toks)
