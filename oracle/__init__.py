@@ -3,11 +3,17 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py``, never by the GPU library or its
 Python binding.  Every function here is the plain definition of one step of
-the layer, computed in fp64 (see the header of ``oracle.c`` for the passages
-of the pages each step follows).
+the layer (see the header of ``oracle.c`` for the passages of the pages each
+step follows).
+
+``oracle.c`` is built twice: ``liboracle.so`` accumulates in fp32 (the
+precision the method fixes; the default, ``PRECISION``), ``liboracle_f64.so``
+in fp64 (a diagnostic of the fp32 build's own rounding).  ``using("fp64")``
+switches the functions below to the diagnostic build inside a ``with`` block.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -15,28 +21,50 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+_SOS = {"fp32": os.path.join(_HERE, "liboracle.so"), "fp64": os.path.join(_HERE, "liboracle_f64.so")}
+_DEFS = {"fp32": [], "fp64": ["-DORC_ACC_FP64"]}
+PRECISION = "fp32"
 
 
 def build() -> str:
     src = os.path.join(_HERE, "oracle.c")
-    tmp = _SO + ".tmp"
-    # -ffp-contract=off: no fused multiply-adds, every product is rounded as written
-    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                           "-ffp-contract=off", src, "-o", tmp, "-lm"])
-    os.replace(tmp, _SO)
-    return _SO
+    for prec, so in _SOS.items():
+        tmp = so + ".tmp"
+        # -ffp-contract=off: no fused multiply-adds, every product is rounded as written
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-ffp-contract=off", *_DEFS[prec], src, "-o", tmp, "-lm"])
+        os.replace(tmp, so)
+    return _SOS["fp32"]
 
 
-_lib = None
+_libs: dict = {}
+_current = [PRECISION]
+
+
+@contextlib.contextmanager
+def using(precision: str):
+    """Run the oracle calls inside the block on the build of `precision`."""
+    assert precision in _SOS, precision
+    old = _current[0]
+    _current[0] = precision
+    try:
+        yield
+    finally:
+        _current[0] = old
+
+
+def precision() -> str:
+    """The accumulation precision the calls run in now (as reported by the build)."""
+    return _load().orc_precision().decode()
 
 
 def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_SO):
+    prec = _current[0]
+    if prec not in _libs:
+        so = _SOS[prec]
+        if not os.path.exists(so):
             build()
-        lib = ctypes.CDLL(_SO)
+        lib = ctypes.CDLL(so)
         p, i32, i64, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_uint
         d = ctypes.c_double
         lib.orc_e2m1.restype = d
@@ -66,8 +94,12 @@ def _load():
         lib.orc_dense_fp8.argtypes = [p, p, p, p, i32, i32, p, i64, p]
         lib.orc_layer_tokens.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p, p, p,
                                          p, i64, p, p, p, p]
-        _lib = lib
-    return _lib
+        lib.orc_layer_pairs.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p, p, p,
+                                        p, i64, p, p, p, p, p]
+        lib.orc_precision.restype = ctypes.c_char_p
+        lib.orc_precision.argtypes = []
+        _libs[prec] = lib
+    return _libs[prec]
 
 
 def _p(a):
@@ -229,6 +261,26 @@ def layer_tokens(inp, tokens=None, want_pairs: bool = False):
     if want_pairs:
         return y, h, hq, hs
     return y
+
+
+def layer_pairs(inp, pairs):
+    """Per-pair intermediates of the layer for (token, slot) pairs p = t*k + j:
+    (expert [n] int32, h [n, I] fp32, hq [n, I], hs [n, I/32], O [n, H] float64
+    holding the build's accumulation-precision values), by the same steps as
+    ``layer_tokens``."""
+    sh = inp.shape
+    H, I, E, k = sh.H, sh.I, sh.E, sh.k
+    pr = _c(pairs, np.int32)
+    n = pr.size
+    ex = np.empty(n, dtype=np.int32)
+    h = np.empty((n, I), dtype=np.float32)
+    hq = np.empty((n, I), dtype=np.uint8)
+    hs = np.empty((n, I // 32), dtype=np.uint8)
+    O = np.empty((n, H), dtype=np.float64)
+    _load().orc_layer_pairs(_p(_c(inp.x, np.uint16)), _p(_c(inp.logits, np.float32)), H, I, E, k,
+                            _p(inp.w1), _p(inp.s1), _p(inp.w3), _p(inp.s3), _p(inp.w2), _p(inp.s2),
+                            _p(pr), n, _p(ex), _p(h), _p(hq), _p(hs), _p(O))
+    return ex, h, hq, hs, O
 
 
 # ------------------------------------------------- router and shared expert

@@ -20,11 +20,16 @@
  * formats and the E8M0 scale are those of the OCP Microscaling (MX) v1.0
  * format family.
  *
- * Arithmetic: every decode is exact; dot products, SwiGLU, softmax and the
- * combine run in fp64 in plain index order.  The one place where a floating
- * value decides an integer code inside the layer (requantising the SwiGLU
- * output h) takes that decision on h rounded to fp32, the precision the GPU
- * kernels hold h in.  Routing compares the fp32 logits themselves.
+ * Arithmetic: every decode is exact.  Dot products, SwiGLU, softmax and the
+ * combine run in plain ascending index order in the accumulation type acc_t:
+ * fp32 by default (the precision the method fixes: products of the decoded
+ * values, which are exact, summed in fp32; exp in fp32), or fp64 when built
+ * with -DORC_ACC_FP64, a diagnostic build that measures the fp32 build's own
+ * rounding.  The one place where a floating value decides an integer code
+ * inside the layer (requantising the SwiGLU output h) takes that decision on
+ * h in fp32, the precision the GPU kernels hold h in, in both builds.
+ * Routing compares the fp32 logits themselves.  The router logits are the
+ * exact sums (fp64) in both builds: they are compared against a bound.
  *
  * Beside the layer: the router logits and the shared expert around it, and
  * the FP8 dense projection (FP8 weights with per-32 E8M0 scales times MXFP8
@@ -36,6 +41,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#ifdef ORC_ACC_FP64
+typedef double acc_t;
+#define ACC_EXP exp
+#define ORC_PRECISION "fp64"
+#else
+typedef float acc_t;
+#define ACC_EXP expf
+#define ORC_PRECISION "fp32"
+#endif
+
+/* The accumulation type this build was compiled with: "fp32" or "fp64". */
+const char* orc_precision(void) { return ORC_PRECISION; }
 
 /* ---------------------------------------------------------------- decoders */
 
@@ -169,7 +187,7 @@ void orc_quant_mxfp8_f32(const float* x, long M, int K, uint8_t* q, uint8_t* s) 
  * logit, ties going to the lower expert index (fixed tie-break on expert id,
  * pwwt.cn review sections 4.1-4.2).  The fp32 logits are compared as fp32
  * values (so -0 equals +0).  Gates are a softmax over the k selected logits:
- * g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0). */
+ * g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), the sum in slot order. */
 void orc_route_token(const float* logit, int E, int k, int32_t* ids, float* gates) {
   unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
   for (int j = 0; j < k; ++j) {
@@ -182,9 +200,10 @@ void orc_route_token(const float* logit, int E, int k, int32_t* ids, float* gate
     ids[j] = best;
   }
   free(taken);
-  double l0 = (double)logit[ids[0]], den = 0.0;
-  for (int j = 0; j < k; ++j) den += exp((double)logit[ids[j]] - l0);
-  for (int j = 0; j < k; ++j) gates[j] = (float)(exp((double)logit[ids[j]] - l0) / den);
+  const acc_t l0 = (acc_t)logit[ids[0]];
+  acc_t den = 0;
+  for (int j = 0; j < k; ++j) den += ACC_EXP((acc_t)logit[ids[j]] - l0);
+  for (int j = 0; j < k; ++j) gates[j] = (float)(ACC_EXP((acc_t)logit[ids[j]] - l0) / den);
 }
 
 void orc_route(const float* logits, long T, int E, int k, int32_t* ids, float* gates) {
@@ -214,31 +233,62 @@ void orc_sort(const int32_t* ids, long P, int E, int32_t* counts, int32_t* offse
 
 /* ------------------------------------------------------------ expert FFN */
 
+/* Row `row` of a packed weight matrix with K elements per row, decoded into
+ * out[0..K): each element is its nibble's e2m1 value (even K index in the low
+ * half of the byte) times its 32-block's E8M0 scale (the product is exact). */
+static void decode_weight_row(const uint8_t* w, const uint8_t* s, int K, long row, acc_t* out) {
+  double e2m1_of[16];
+  for (unsigned n = 0; n < 16; ++n) e2m1_of[n] = orc_e2m1(n);
+  for (int b = 0; b < K / 32; ++b) {
+    const double scale = orc_e8m0(s[row * (K / 32) + b]);
+    for (int c = 32 * b; c < 32 * b + 32; ++c) {
+      const uint8_t byte = w[row * (K / 2) + c / 2];
+      const unsigned nib = (c & 1) ? (byte >> 4) : (byte & 15u);
+      out[c] = (acc_t)(e2m1_of[nib] * scale);
+    }
+  }
+}
+
 /* Gate/up projections of one MXFP8 activation row through expert weights
- * W1, W3 ([I, H] packed): G[i] = sum_h x[h] W1[i,h], U[i] likewise with W3. */
+ * W1, W3 ([I, H] packed): G[i] = sum_h x[h] W1[i,h], U[i] likewise with W3,
+ * summed in ascending h in acc_t (each product of an e4m3 and an e2m1 value
+ * with power-of-two scales is exact in either type).  G, U are returned as
+ * doubles holding the acc_t values. */
 void orc_expert_gate_up(const uint8_t* xq, const uint8_t* xs, int H, int I,
                         const uint8_t* w1, const uint8_t* s1,
                         const uint8_t* w3, const uint8_t* s3, double* G, double* U) {
-  double* xd = (double*)malloc(sizeof(double) * (size_t)H);
-  for (int h = 0; h < H; ++h) xd[h] = orc_e4m3(xq[h]) * orc_e8m0(xs[h / 32]);
-#pragma omp parallel for schedule(static)
-  for (int i = 0; i < I; ++i) {
-    double g = 0.0, u = 0.0;
-    for (int h = 0; h < H; ++h) {
-      g += xd[h] * weight_elem(w1, s1, H, i, h);
-      u += xd[h] * weight_elem(w3, s3, H, i, h);
+  acc_t* xd = (acc_t*)malloc(sizeof(acc_t) * (size_t)H);
+  for (int h = 0; h < H; ++h) xd[h] = (acc_t)(orc_e4m3(xq[h]) * orc_e8m0(xs[h / 32]));
+#pragma omp parallel
+  {
+    acc_t* r1 = (acc_t*)malloc(sizeof(acc_t) * (size_t)H);
+    acc_t* r3 = (acc_t*)malloc(sizeof(acc_t) * (size_t)H);
+#pragma omp for schedule(static)
+    for (int i = 0; i < I; ++i) {
+      decode_weight_row(w1, s1, H, i, r1);
+      decode_weight_row(w3, s3, H, i, r3);
+      acc_t g = 0, u = 0;
+      for (int h = 0; h < H; ++h) {
+        g += xd[h] * r1[h];
+        u += xd[h] * r3[h];
+      }
+      G[i] = (double)g;
+      U[i] = (double)u;
     }
-    G[i] = g;
-    U[i] = u;
+    free(r1);
+    free(r3);
   }
   free(xd);
 }
 
-/* SwiGLU h = silu(G) * U with silu(z) = z / (1 + e^-z), then MXFP8
- * requantisation of h per 32 along I.  h is rounded to fp32 first. */
+/* SwiGLU h = silu(G) * U with silu(z) = z / (1 + e^-z), evaluated in acc_t,
+ * then MXFP8 requantisation of h per 32 along I.  h is rounded to fp32 first. */
 void orc_swiglu_requant(const double* G, const double* U, int I, float* h,
                         uint8_t* hq, uint8_t* hs) {
-  for (int i = 0; i < I; ++i) h[i] = (float)(G[i] / (1.0 + exp(-G[i])) * U[i]);
+  for (int i = 0; i < I; ++i) {
+    const acc_t g = (acc_t)G[i], u = (acc_t)U[i];
+    h[i] = (float)(g / ((acc_t)1 + ACC_EXP(-g)) * u);
+  }
   double v[32];
   for (int b = 0; b < I / 32; ++b) {
     for (int i = 0; i < 32; ++i) v[i] = (double)h[b * 32 + i];
@@ -246,16 +296,23 @@ void orc_swiglu_requant(const double* G, const double* U, int I, float* h,
   }
 }
 
-/* Down projection: O[r] = sum_i h[i] W2[r,i], W2 packed [H, I]. */
+/* Down projection: O[r] = sum_i h[i] W2[r,i], W2 packed [H, I], summed in
+ * ascending i in acc_t. */
 void orc_expert_down(const uint8_t* hq, const uint8_t* hs, int H, int I,
                      const uint8_t* w2, const uint8_t* s2, double* O) {
-  double* hd = (double*)malloc(sizeof(double) * (size_t)I);
-  for (int i = 0; i < I; ++i) hd[i] = orc_e4m3(hq[i]) * orc_e8m0(hs[i / 32]);
-#pragma omp parallel for schedule(static)
-  for (int r = 0; r < H; ++r) {
-    double o = 0.0;
-    for (int i = 0; i < I; ++i) o += hd[i] * weight_elem(w2, s2, I, r, i);
-    O[r] = o;
+  acc_t* hd = (acc_t*)malloc(sizeof(acc_t) * (size_t)I);
+  for (int i = 0; i < I; ++i) hd[i] = (acc_t)(orc_e4m3(hq[i]) * orc_e8m0(hs[i / 32]));
+#pragma omp parallel
+  {
+    acc_t* r2 = (acc_t*)malloc(sizeof(acc_t) * (size_t)I);
+#pragma omp for schedule(static)
+    for (int r = 0; r < H; ++r) {
+      decode_weight_row(w2, s2, I, r, r2);
+      acc_t o = 0;
+      for (int i = 0; i < I; ++i) o += hd[i] * r2[i];
+      O[r] = (double)o;
+    }
+    free(r2);
   }
   free(hd);
 }
@@ -284,18 +341,18 @@ void orc_layer_tokens(const uint16_t* x, const float* logits, int H, int I, int 
   uint8_t* hq = (uint8_t*)malloc((size_t)I);
   uint8_t* hs = (uint8_t*)malloc((size_t)I / 32);
   double* O = (double*)malloc(sizeof(double) * (size_t)H);
-  double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+  acc_t* acc = (acc_t*)malloc(sizeof(acc_t) * (size_t)H);
   for (long n = 0; n < ntok; ++n) {
     long t = tokens[n];
     orc_route_token(logits + t * E, E, k, ids, gates);
     orc_quant_mxfp8_bf16(x + t * (long)H, 1, H, xq, xs);
-    for (int r = 0; r < H; ++r) acc[r] = 0.0;
+    for (int r = 0; r < H; ++r) acc[r] = 0;
     for (int j = 0; j < k; ++j) {
       size_t e = (size_t)ids[j];
       orc_expert_gate_up(xq, xs, H, I, w1 + e * wup, s1 + e * sup, w3 + e * wup, s3 + e * sup, G, U);
       orc_swiglu_requant(G, U, I, h, hq, hs);
       orc_expert_down(hq, hs, H, I, w2 + e * wdn, s2 + e * sdn, O);
-      for (int r = 0; r < H; ++r) acc[r] += (double)gates[j] * O[r];
+      for (int r = 0; r < H; ++r) acc[r] += (acc_t)gates[j] * (acc_t)O[r];
       if (h_out) memcpy(h_out + ((size_t)n * k + j) * I, h, sizeof(float) * (size_t)I);
       if (hq_out) memcpy(hq_out + ((size_t)n * k + j) * I, hq, (size_t)I);
       if (hs_out) memcpy(hs_out + ((size_t)n * k + j) * (I / 32), hs, (size_t)I / 32);
@@ -304,6 +361,47 @@ void orc_layer_tokens(const uint16_t* x, const float* logits, int H, int I, int 
   }
   free(ids); free(gates); free(xq); free(xs); free(G); free(U);
   free(h); free(hq); free(hs); free(O); free(acc);
+}
+
+/* The layer's per-pair intermediates for a list of (token, slot) pairs
+ * p = t*k + j, by the same steps as orc_layer_tokens: route token t, take its
+ * slot-j expert e, quantise x_t, run that expert's gate/up projections,
+ * SwiGLU and requantisation, and its down projection.  Per listed pair n:
+ * expert[n] = e, h[n, I] (fp32), hq[n, I], hs[n, I/32], and O[n, H] (the
+ * down projection before the gate, as doubles holding acc_t values).  The
+ * outputs may be NULL except O. */
+void orc_layer_pairs(const uint16_t* x, const float* logits, int H, int I, int E, int k,
+                     const uint8_t* w1, const uint8_t* s1, const uint8_t* w3, const uint8_t* s3,
+                     const uint8_t* w2, const uint8_t* s2, const int32_t* pairs, long npairs,
+                     int32_t* expert_out, float* h_out, uint8_t* hq_out, uint8_t* hs_out,
+                     double* O) {
+  const size_t wup = (size_t)I * (H / 2), sup = (size_t)I * (H / 32);
+  const size_t wdn = (size_t)H * (I / 2), sdn = (size_t)H * (I / 32);
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  float* gates = (float*)malloc(sizeof(float) * (size_t)k);
+  uint8_t* xq = (uint8_t*)malloc((size_t)H);
+  uint8_t* xs = (uint8_t*)malloc((size_t)H / 32);
+  double* G = (double*)malloc(sizeof(double) * (size_t)I);
+  double* U = (double*)malloc(sizeof(double) * (size_t)I);
+  float* h = (float*)malloc(sizeof(float) * (size_t)I);
+  uint8_t* hq = (uint8_t*)malloc((size_t)I);
+  uint8_t* hs = (uint8_t*)malloc((size_t)I / 32);
+  for (long n = 0; n < npairs; ++n) {
+    const long t = pairs[n] / k;
+    const int j = (int)(pairs[n] % k);
+    orc_route_token(logits + t * E, E, k, ids, gates);
+    orc_quant_mxfp8_bf16(x + t * (long)H, 1, H, xq, xs);
+    const size_t e = (size_t)ids[j];
+    orc_expert_gate_up(xq, xs, H, I, w1 + e * wup, s1 + e * sup, w3 + e * wup, s3 + e * sup, G, U);
+    orc_swiglu_requant(G, U, I, h, hq, hs);
+    orc_expert_down(hq, hs, H, I, w2 + e * wdn, s2 + e * sdn, O + (size_t)n * H);
+    if (expert_out) expert_out[n] = (int32_t)e;
+    if (h_out) memcpy(h_out + (size_t)n * I, h, sizeof(float) * (size_t)I);
+    if (hq_out) memcpy(hq_out + (size_t)n * I, hq, (size_t)I);
+    if (hs_out) memcpy(hs_out + (size_t)n * (I / 32), hs, (size_t)I / 32);
+  }
+  free(ids); free(gates); free(xq); free(xs); free(G); free(U);
+  free(h); free(hq); free(hs);
 }
 
 /* --------------------------------------------- router and shared expert */
@@ -354,24 +452,24 @@ void orc_layer_tokens_shared(const uint16_t* x, const float* logits, int H, int 
   uint8_t* hq = (uint8_t*)malloc((size_t)Imax);
   uint8_t* hs = (uint8_t*)malloc((size_t)Imax / 32);
   double* O = (double*)malloc(sizeof(double) * (size_t)H);
-  double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+  acc_t* acc = (acc_t*)malloc(sizeof(acc_t) * (size_t)H);
   for (long n = 0; n < ntok; ++n) {
     long t = tokens[n];
     orc_route_token(logits + t * E, E, k, ids, gates);
     orc_quant_mxfp8_bf16(x + t * (long)H, 1, H, xq, xs);
-    for (int r = 0; r < H; ++r) acc[r] = 0.0;
+    for (int r = 0; r < H; ++r) acc[r] = 0;
     for (int j = 0; j < k; ++j) {
       size_t e = (size_t)ids[j];
       orc_expert_gate_up(xq, xs, H, I, w1 + e * wup, s1 + e * sup, w3 + e * wup, s3 + e * sup, G, U);
       orc_swiglu_requant(G, U, I, h, hq, hs);
       orc_expert_down(hq, hs, H, I, w2 + e * wdn, s2 + e * sdn, O);
-      for (int r = 0; r < H; ++r) acc[r] += (double)gates[j] * O[r];
+      for (int r = 0; r < H; ++r) acc[r] += (acc_t)gates[j] * (acc_t)O[r];
     }
     if (w1s) {
       orc_expert_gate_up(xq, xs, H, Is, w1s, s1s, w3s, s3s, G, U);
       orc_swiglu_requant(G, U, Is, h, hq, hs);
       orc_expert_down(hq, hs, H, Is, w2s, s2s, O);
-      for (int r = 0; r < H; ++r) acc[r] += O[r];
+      for (int r = 0; r < H; ++r) acc[r] += (acc_t)O[r];
     }
     for (int r = 0; r < H; ++r) y[n * (long)H + r] = (float)acc[r];
   }
@@ -387,26 +485,27 @@ void orc_layer_tokens_shared(const uint16_t* x, const float* logits, int H, int 
  * way FP8 pays off).  Weights W [N, K] are OCP e4m3 codes with one E8M0 scale per 32
  * consecutive K elements of a row, activations the MXFP8 rows xq/xs of the
  * path's own quantiser; y[t, n] = sum_k x[t, k] * W[n, k] over the decoded
- * values, summed in fp64 in index order (each product of two scaled e4m3
- * values is exact in fp64).  tokens lists the rows of x to compute; y is
+ * values, summed in acc_t in index order (each product of two scaled e4m3
+ * values is exact in fp64; in fp32 too while the product's scale stays in
+ * the normal range, as at every scale the path produces).  tokens lists the rows of x to compute; y is
  * [ntok, N]. */
 void orc_dense_fp8(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                    int N, int K, const int32_t* tokens, long ntok, double* y) {
-  double* xd = (double*)malloc(sizeof(double) * (size_t)ntok * (size_t)K);
+  acc_t* xd = (acc_t*)malloc(sizeof(acc_t) * (size_t)ntok * (size_t)K);
   for (long i = 0; i < ntok; ++i) {
     const long t = tokens[i];
     for (int k = 0; k < K; ++k)
-      xd[i * K + k] = orc_e4m3(xq[t * K + k]) * orc_e8m0(xs[t * (K / 32) + k / 32]);
+      xd[i * K + k] = (acc_t)(orc_e4m3(xq[t * K + k]) * orc_e8m0(xs[t * (K / 32) + k / 32]));
   }
 #pragma omp parallel for schedule(static)
   for (int n = 0; n < N; ++n) {
-    double* wd = (double*)malloc(sizeof(double) * (size_t)K);
+    acc_t* wd = (acc_t*)malloc(sizeof(acc_t) * (size_t)K);
     for (int k = 0; k < K; ++k)
-      wd[k] = orc_e4m3(wq[(long)n * K + k]) * orc_e8m0(ws[(long)n * (K / 32) + k / 32]);
+      wd[k] = (acc_t)(orc_e4m3(wq[(long)n * K + k]) * orc_e8m0(ws[(long)n * (K / 32) + k / 32]));
     for (long i = 0; i < ntok; ++i) {
-      double acc = 0.0;
+      acc_t acc = 0;
       for (int k = 0; k < K; ++k) acc += xd[i * K + k] * wd[k];
-      y[i * N + n] = acc;
+      y[i * N + n] = (double)acc;
     }
     free(wd);
   }

@@ -10,9 +10,20 @@
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 import synth
+
+# unit roundoff of each oracle build (round to nearest)
+UNIT = {"fp32": Fraction(1, 2 ** 24), "fp64": Fraction(1, 2 ** 53)}
+
+
+def gamma(n: int, u: Fraction) -> Fraction:
+    """The classic bound of recursive summation: |fl(sum a_i) - sum a_i| <=
+    gamma_(n-1) * sum |a_i|, gamma_n = n u / (1 - n u) (Higham, Accuracy and
+    Stability of Numerical Algorithms, section 4.2)."""
+    return n * u / (1 - n * u)
 
 
 def _e4m3_frac(b: int) -> Fraction:
@@ -28,17 +39,23 @@ def _e8m0_frac(c: int) -> Fraction:
     return Fraction(2) ** (c - 127)
 
 
-def test_dense_exact_brute_force():
+@pytest.mark.parametrize("prec", ["fp32", "fp64"])
+def test_dense_exact_brute_force(prec):
+    """Each product of two scaled e4m3 values is exact, so the only error is the
+    summation's: within gamma_(K-1) * sum |products| of the exact rational sum."""
     inp = synth.make_dense_inputs("d0", T=3, K=64, N=5)
     xq, xs = oracle.quant_mxfp8_bf16(inp.x)
-    y = oracle.dense_fp8(xq, xs, inp.wq, inp.ws)
+    with oracle.using(prec):
+        y = oracle.dense_fp8(xq, xs, inp.wq, inp.ws)
     assert y.shape == (3, 5)
     for t in range(3):
         for n in range(5):
-            exact = sum(_e4m3_frac(int(xq[t, k])) * _e8m0_frac(int(xs[t, k // 32]))
-                        * _e4m3_frac(int(inp.wq[n, k])) * _e8m0_frac(int(inp.ws[n, k // 32]))
-                        for k in range(64))
-            assert abs(Fraction(y[t, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50), (t, n)
+            prods = [_e4m3_frac(int(xq[t, k])) * _e8m0_frac(int(xs[t, k // 32]))
+                     * _e4m3_frac(int(inp.wq[n, k])) * _e8m0_frac(int(inp.ws[n, k // 32]))
+                     for k in range(64)]
+            exact = sum(prods)
+            bound = gamma(63, UNIT[prec]) * sum(abs(v) for v in prods)
+            assert abs(Fraction(y[t, n]) - exact) <= bound, (t, n)
 
 
 def test_dense_one_hot_weights_give_the_activations():
