@@ -43,6 +43,7 @@ HBM_PEAK_GBS = 8000.0
 DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true, 1>"   # the instantiations the library launches
 DENSE_PREFILL_KERNEL = "dense_prefill_kernel<2, 4, 6, 2, 1>"  # (prefill: the 192 x 256 tile)
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 (and FP8 x FP4 scaled MFMA at the FP8 issue rate)
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense FP4 x FP4 (reported beside: the mixed FP8 x FP4 MFMA issues at the FP8 rate)
 METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU"
 
 
@@ -256,23 +257,31 @@ def copy_calibration(reps: int = 20):
     torch.cuda.synchronize()
 
 
+def oracle_threads() -> int:
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return min(threads, len(os.sched_getaffinity(0)))
+
+
 def cpu_baseline(name: str, budget_s: float):
+    """The oracle as it stands on a bounded sample of the workload: whole-layer
+    rows (route, MXFP8 of x, the k expert FFNs, combine) of tokens drawn without
+    replacement by a seeded generator, one token per call, until `budget_s` of
+    wall time is spent (at least one token).  tokens/s = tokens done / time."""
     import oracle
     import synth
     inp = synth.make_inputs(name)
     T = inp.shape.T
-    oracle.layer_tokens(inp, np.arange(1, dtype=np.int32))  # warm the page cache
+    order = np.random.default_rng(12345).permutation(T).astype(np.int32)
+    oracle.layer_tokens(inp, order[:1])  # warm the page cache of the weights
     n_tok = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        oracle.layer_tokens(inp)
-        n_tok += T
+    while n_tok == 0 or time.perf_counter() - t0 < budget_s:
+        oracle.layer_tokens(inp, order[n_tok % T:n_tok % T + 1])
+        n_tok += 1
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    threads = min(threads, len(os.sched_getaffinity(0)))
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole layer, all {T} tokens of the {name} workload, repeated "
-                      f"{n_tok // T}x in {dt:.1f} s (fp64 plain C, OpenMP)"}
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{n_tok} of the {T} tokens of the {name} workload (seeded random draw), whole layer "
+                      f"per token in {dt:.1f} s ({oracle.PRECISION} plain C, OpenMP over output rows)"}
 
 
 def cpu_baseline_dense(name: str, budget_s: float):
@@ -286,9 +295,7 @@ def cpu_baseline_dense(name: str, budget_s: float):
         oracle.dense_fp8(xq, xs, inp.wq, inp.ws, np.array([n_tok % inp.shape.T], dtype=np.int32))
         n_tok += 1
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    threads = min(threads, len(os.sched_getaffinity(0)))
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
             "sample": f"{n_tok} single-token rows of the {name} projection in {dt:.1f} s "
                       f"(fp64 plain C, OpenMP over the output rows; x quantised beforehand)"}
 
@@ -459,11 +466,14 @@ def bench_shard(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c1",
-                    help="workload name: c0-c4 the MoE layer (c1 is the measured one), d0-d3 the FP8 "
-                         "dense projection")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c4",
+                    help="workload name: c0-c4 the MoE layer (c4, the largest, is the headline), d0-d3 "
+                         "the FP8 dense projection")
+    ap.add_argument("--decode-leg", default="c1",
+                    help="layer workload timed after the main one in the same process and reported "
+                         "as decode_leg (the metric's HBM-bound part); '' = none")
     ap.add_argument("--flags", type=int, default=0, help="1 = force decode path, 2 = force prefill path")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 = skip")
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0 = auto)")
@@ -511,13 +521,34 @@ def main():
         bench_shard(args)
         return
 
+    line = measure_layer(args, args.config, args.steps, args.warmup)
+    if args.decode_leg and args.config != args.decode_leg and not args.shard:
+        # the decode-shaped leg of the metric (achieved HBM TB/s), same process,
+        # after the prefill-shaped workload's memory is released
+        import torch
+        torch.cuda.empty_cache()
+        d = measure_layer(args, args.decode_leg, args.steps, args.warmup)
+        line["decode_leg"] = {
+            "workload": d["config"]["workload"], "value": d["value"], "unit": d["unit"],
+            "ms_per_step": d["ms_per_step"], "step_ms_p10_p50_p90": d["step_ms_p10_p50_p90"],
+            "layer_hbm_tbps": d["layer_hbm_tbps"], "layer_hbm_frac": d["layer_hbm_frac"],
+            "used_experts": d["config"]["used_experts"], "roofline": d["roofline"]}
+    if args.copy_calibration:
+        copy_calibration()
+    line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget) if args.cpu_budget > 0 else None
+    print(json.dumps(line), flush=True)
+
+
+def measure_layer(args, cfg: str, steps: int, warmup: int) -> dict:
+    """Time `steps` layer steps of workload `cfg` after `warmup` untimed ones;
+    returns the JSON line's fields (cpu_baseline aside)."""
     import torch
 
     import fp4_routed_expert_amd as moe
     import synth
 
     dev = torch.device("cuda:0")
-    inp = synth.make_inputs(args.config)
+    inp = synth.make_inputs(cfg)
     sh = inp.shape
     T, H, I, E, k = sh.T, sh.H, sh.I, sh.E, sh.k
     # --full: ns shared experts packed after the E routed ones, every token's
@@ -536,6 +567,7 @@ def main():
     del canon
     x = t(inp.x.view(np.int16)).view(torch.bfloat16)
     logits = t(inp.logits)
+    del inp
     if args.full:
         # router weights, one copy per weight copy
         wg = [t(synth.make_router_weights(sh).view(np.int16)).view(torch.bfloat16) for _ in range(copies)]
@@ -561,9 +593,9 @@ def main():
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, kk, Ew, H, I), 256),
                            dtype=torch.uint8, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     ev_r = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)]
+            for _ in range(steps)]
     if args.full:
         lws = torch.empty(max(moe.layer_full_workspace_size(T, k, Ew, H, I, ns, args.flags), 256),
                           dtype=torch.uint8, device=dev)
@@ -597,7 +629,7 @@ def main():
         moe.expert_down(pw, hq, hs, offsets, T, kk, args.flags, O=O, workspace=stage_ws)
         moe.combine(O, gates, pp, T, kk, H, y=y)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     if args.graph:
@@ -609,35 +641,35 @@ def main():
             with torch.cuda.graph(g):
                 step(c)
             graphs.append(g)
-        for i in range(args.warmup):
+        for i in range(warmup):
             graphs[i % copies].replay()
         torch.cuda.synchronize()
 
         def step(i):  # noqa: F811
             graphs[i % copies].replay()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dt = t1 - t0
-    for i in range(args.steps):
-        staged_step(args.warmup + i, i)
+    for i in range(steps):
+        staged_step(warmup + i, i)
     torch.cuda.synchronize()
     up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     # the spread of single steps: each layer call bracketed by its own events
     # (a separate loop, outside the timed region)
-    for i in range(args.steps):
+    for i in range(steps):
         ev[i][0].record()
-        step(args.warmup + i)
+        step(warmup + i)
         ev[i][1].record()
     torch.cuda.synchronize()
     step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     counts = sort_out[0].cpu().numpy()
     used = int((counts > 0).sum())
 
-    ms_per_step = dt / args.steps * 1e3
-    tokens_per_s = T * args.steps / dt
+    ms_per_step = dt / steps * 1e3
+    tokens_per_s = T * steps / dt
     # algorithmic bytes: weights of the experts that tokens were routed to, plus activations
     b_layer = used * weight_bytes_per_expert(H, I, 3) + T * H * 2 + T * E * 4 + T * H * 4
     b_up = used * weight_bytes_per_expert(H, I, 2) + T * H * (1 + 1 / 32) + P * I * (1 + 1 / 32)
@@ -645,35 +677,37 @@ def main():
     flops = 6.0 * H * I * P
     up_flops = 4.0 * H * I * P
     prefill = args.flags == 2 or (args.flags == 0 and P > 16 * Ew)
+    wl = synth.CONFIG_NAMES.get(cfg, cfg)
     if prefill:
         achieved = up_flops / (up_ms * 1e-3) / 1e12
         kname = "prefill_gemm_kernel<true>"
         roof = {"bound": "mfma", "kernel": kname + " (gate/up GEMM + SwiGLU + MXFP8 of h)",
                 "achieved": achieved, "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_FP8_PEAK_TFLOPS,
-                "traffic": load_traffic(kname, synth.CONFIG_NAMES.get(args.config, args.config)),
+                "frac_of_fp4_peak": achieved / MFMA_FP4_PEAK_TFLOPS,
+                "traffic": load_traffic(kname, wl),
                 "alg_flops_per_launch": up_flops, "avg_launch_us": up_ms * 1e3}
     else:
         kname = "up_decode_kernel<1>"
         roof = {"bound": "hbm", "kernel": kname + " (gate/up GEMM + SwiGLU + MXFP8 of h)",
                 "achieved": up_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": up_gbs / HBM_PEAK_GBS,
-                "traffic": load_traffic(kname, synth.CONFIG_NAMES.get(args.config, args.config)),
+                "traffic": load_traffic(kname, wl),
                 "alg_bytes_per_launch": b_up, "avg_launch_us": up_ms * 1e3}
     line = {
         "metric": METRIC,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp4e2m1xfp8e4m3->fp32",
         "data": "synthetic",
-        "config": {"workload": synth.CONFIG_NAMES.get(args.config, args.config), "T": T, "H": H, "I": I,
+        "config": {"workload": wl, "T": T, "H": H, "I": I,
                    "E": E, "k": k, "seed": sh.seed, "used_experts": used, "weight_copies": copies,
                    "path_flags": args.flags, "launch": "hip_graph" if args.graph else "eager"},
         "step_ms_p10_p50_p90": [float(v) for v in np.percentile(step_ms, [10, 50, 90])],
@@ -695,13 +729,7 @@ def main():
                           "alg_flops_per_launch": 2.0 * T * H * E, "avg_launch_us": r_ms * 1e3}
         line["layer_hbm_tbps"] = (b_layer + E * H * 2) / (ms_per_step * 1e-3) / 1e12
         line["layer_hbm_frac"] = line["layer_hbm_tbps"] * 1e3 / HBM_PEAK_GBS
-    if args.copy_calibration:
-        copy_calibration()
-    if args.cpu_budget > 0:
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
-    else:
-        line["cpu_baseline"] = None
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":

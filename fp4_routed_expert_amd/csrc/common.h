@@ -18,11 +18,14 @@ constexpr int kWave = 64;
 // X = floor(log2 amax) - 8, X = -127 when amax is zero or below the fp32
 // normal range, scale code X + 127.  Returned: the scale code; *mul is the
 // exact power of two 2^-X to multiply each element by before rounding.
-__device__ __forceinline__ uint32_t mx_scale_from_amax(float amax, float* mul) {
-  const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFFu;  // amax >= 0
+__host__ __device__ __forceinline__ uint32_t mx_scale_from_amax(float amax, float* mul) {
+  uint32_t ua;
+  __builtin_memcpy(&ua, &amax, 4);
+  const uint32_t ef = (ua >> 23) & 0xFFu;  // amax >= 0
   int X = (ef == 0u) ? -127 : (int)ef - 135;
   if (X < -127) X = -127;  // ef <= 254 keeps X <= 119
-  *mul = __uint_as_float((uint32_t)(127 - X) << 23);
+  const uint32_t um = (uint32_t)(127 - X) << 23;
+  __builtin_memcpy(mul, &um, 4);
   return (uint32_t)(X + 127);
 }
 

@@ -157,3 +157,22 @@ def test_dense_one_hot_is_exact(flags, dev):
     xq, xs = oracle.quant_mxfp8_bf16(inp.x)
     want = oracle.decode_mxfp8(xq, xs)[:, cols]         # 4 significant bits: exact in bf16
     assert np.array_equal(y, want.astype(np.float32))
+
+
+@pytest.mark.parametrize("T", [17, 33, 96])
+def test_dense_streaming_two_token_tiles_long_k(T, dev):
+    """The weight-streaming kernel from 17 tokens takes two 16-token tiles per
+    pass over the weights; with K = 8192 (64 K-steps, more than its 16 waves)
+    every wave runs whole batches of its K loop, with a ragged (T = 17, 33) or
+    full (T = 96) second tile.  All tokens against the oracle and against the
+    tiled GEMM."""
+    c = get_dense("d0", dev, T=T, K=8192, N=256)
+    log(f"[dense] streaming, two token tiles, T{T} K8192 N256")
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    y = moe.dense_forward(c.dw, xq, xs)            # the default path: streaming up to T = 96
+    y_pre = moe.dense_forward(c.dw, xq, xs, PRE)
+    torch.cuda.synchronize()
+    toks = np.arange(T, dtype=np.int32)
+    ref = c.ref(toks)
+    check_y(y.float().cpu().numpy(), ref, f"dense/stream2/T{T}")
+    check_y(y.float().cpu().numpy(), y_pre.float().cpu().numpy(), f"dense/stream2-vs-tiled/T{T}")
