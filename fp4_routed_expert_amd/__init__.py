@@ -22,7 +22,8 @@ from ._lib import (MOE_FLAG_FORCE_DECODE, MOE_FLAG_FORCE_PREFILL, MoeError,  # n
 __all__ = [
     "route_topk", "sort_permute", "quant_act_mxfp8", "prepack_weights", "PackedWeights",
     "expert_up", "expert_down", "combine", "grouped_forward", "moe_layer",
-    "forward_workspace_size", "layer_forward", "layer_workspace_size", "router_logits",
+    "forward_workspace_size", "layer_forward", "layer_workspace_size", "layer_forward_noalloc",
+    "router_logits",
     "router_workspace_size",
     "shared_workspace_size", "shared_expert", "combine_shared", "layer_full_workspace_size",
     "layer_forward_full", "DenseWeights", "dense_prepack", "dense_forward", "dense_layer",
@@ -233,6 +234,21 @@ def layer_forward(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: i
     _lib.check(_lib.lib().moe_fp4_layer_forward(
         ctypes.byref(pw.desc), _ptr(x), _ptr(logits), T, k, _ptr(y), _ptr(workspace),
         workspace.numel(), flags, _stream(x)), "moe_fp4_layer_forward")
+    return y
+
+
+def layer_forward_noalloc(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: int,
+                          flags: int = 0, y=None):
+    """The whole layer with the library's fixed per-GPU scratch as workspace
+    (moe_fp4_layer_forward_noalloc): the call allocates nothing itself."""
+    _check_dtype(x, (torch.bfloat16, torch.int16, torch.uint16), "x")
+    _check_dtype(logits, (torch.float32,), "logits")
+    T, H = x.shape
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _lib.check(_lib.lib().moe_fp4_layer_forward_noalloc(
+        ctypes.byref(pw.desc), _ptr(x), _ptr(logits), T, k, _ptr(y), flags, _stream(x)),
+        "moe_fp4_layer_forward_noalloc")
     return y
 
 

@@ -22,6 +22,7 @@ MOE_FLAG_FORCE_DECODE = 1
 MOE_FLAG_FORCE_PREFILL = 2
 MOE_FP4_LAYOUT_VERSION = 1
 MOE_FP8_DENSE_LAYOUT_VERSION = 1
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeFp4Weights(ctypes.Structure):
@@ -79,6 +80,7 @@ SIGNATURES = {
                                                _U32, _P]),
     "moe_fp4_layer_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _U32]),
     "moe_fp4_layer_forward": (ctypes.c_int, [_WP, _P, _P, _I32, _I32, _P, _P, _SZ, _U32, _P]),
+    "moe_fp4_layer_forward_noalloc": (ctypes.c_int, [_WP, _P, _P, _I32, _I32, _P, _U32, _P]),
     "moe_router_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "moe_router_logits": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "moe_fp4_shared_workspace_size": (_SZ, [_I32, _I32, _I32, _U32]),

@@ -1,6 +1,8 @@
 // C ABI of the library (declared in include/moe_fp4.h): host-side argument
 // checks, workspace carving and path selection.  Every check runs before any
 // launch, so a failing call enqueues nothing and touches no output.
+#include <atomic>
+
 #include "common.h"
 #include "../../include/moe_fp4.h"
 
@@ -407,6 +409,63 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w, const uint16_t* x
                                  reinterpret_cast<const int32_t*>(ws + c.sorted),
                                  reinterpret_cast<const int32_t*>(ws + c.pos), T, k, y, ws + c.fwd,
                                  c.fwd_bytes, flags, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- the no-allocation layer
+// The workspace of moe_fp4_layer_forward_noalloc: a fixed array in device
+// memory, one copy per GPU, held until the process ends.  In host code its
+// name is only a stand-in for the symbol; kernels get its device address,
+// fetched once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device (the first call on a
+// device looks it up; concurrent first calls store the same address).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_fp4_layer_forward_noalloc(const moe_fp4_weights_t* w, const uint16_t* x_bf16,
+                                           const float* logits, int32_t T, int32_t k, float* y,
+                                           uint32_t flags, hipStream_t stream) {
+  moe_status_t st = check_weights(w);
+  if (st != MOE_OK) return st;
+  st = check_tek(T, w->E, k);
+  if (st != MOE_OK) return st;
+  if (select_path((int64_t)T * k, w->E, flags) < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !logits || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_bf16, 16) || !aligned(logits, 4) || !aligned(y, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = layer_carve(T, k, w->E, w->H, w->I).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = hip_status(scratch_address(&ws));
+  if (st != MOE_OK) return st;
+  return moe_fp4_layer_forward(w, x_bf16, logits, T, k, y, ws, MOE_NOALLOC_SCRATCH_BYTES, flags,
+                               stream);
 }
 
 }  // extern "C"

@@ -242,6 +242,32 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w /*(host)*/,
                                    uint32_t flags, hipStream_t stream);
 
 /*
+ * The whole layer as moe_fp4_layer_forward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The intermediates live in a fixed scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES in device memory that the library holds on each
+ * GPU it runs on until the process ends (its address is looked up on the
+ * first call on a device).  The call allocates, frees and clears nothing; the
+ * caller passes inputs and outputs only.  Results are bitwise those of
+ * moe_fp4_layer_forward on the same inputs.
+ *  - Shapes whose moe_fp4_layer_workspace_size(T, k, E, H, I, flags) exceeds
+ *    MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE, nothing enqueued
+ *    (64 MiB holds T <= 476 at H7168 I2048 E256 top-8, T <= 1052 at H4096
+ *    I1536 E64 top-6).
+ *  - Every call on a GPU uses that GPU's one scratch array and leaves its
+ *    contents behind (none is read before the call writes it): calls that
+ *    overlap on one GPU -- other streams, other host threads -- race, and the
+ *    caller must order them.
+ *  - x_bf16 [T, H] bf16 bits (16-byte aligned); logits [T, E] fp32;
+ *    y [T, H] fp32 (out, overwritten, 16-byte aligned); flags as above.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_fp4_layer_forward_noalloc(const moe_fp4_weights_t* w /*(host)*/,
+                                           const uint16_t* x_bf16, const float* logits,
+                                           int32_t T, int32_t k, float* y, uint32_t flags,
+                                           hipStream_t stream);
+
+/*
  * Router logits, the gate network's first layer ahead of step 1:
  * logits[t,e] = sum_h x[t,h] * Wg[e,h], x and Wg bf16, products accumulated
  * in fp32 by the bf16 matrix cores (the pwwt.cn review, section 4.1, lets the

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     so = ctypes.CDLL(_lib.SO_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -235,3 +235,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_noalloc_argument_errors():
+    """The no-allocation layer rejects bad arguments and shapes beyond its fixed
+    scratch before any HIP call (no device here)."""
+    w = _lib.MoeFp4Weights(E=256, H=7168, I=2048, layout_version=_lib.MOE_FP4_LAYOUT_VERSION,
+                           packed=A.value, packed_bytes=1 << 40)
+    f = L.moe_fp4_layer_forward_noalloc
+    wp = ctypes.byref(w)
+    assert f(None, A, A, 8, 8, A, 0, NUL) == INV
+    assert f(wp, NUL, A, 8, 8, A, 0, NUL) == INV
+    assert f(wp, A, A, 8, 8, MIS, 0, NUL) == INV
+    assert f(wp, A, A, 8, 8, A, 3, NUL) == INV                  # both paths forced
+    assert f(wp, A, A, 8, 300, A, 0, NUL) == UNS                # k > 32
+    assert f(wp, A, A, 0, 8, NUL, 0, NUL) == 0                  # T = 0: no-op
+    assert L.moe_fp4_layer_workspace_size(477, 8, 256, 7168, 2048, 0) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(wp, A, A, 477, 8, A, 0, NUL) == WSE                # beyond the fixed scratch
