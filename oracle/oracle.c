@@ -90,18 +90,25 @@ double orc_bf16(uint16_t bits) {
   return (double)f;
 }
 
-/* One element of a packed weight matrix with K elements per row:
- * nibble (even K index in the low half of the byte) times its block scale. */
-static double weight_elem(const uint8_t* w, const uint8_t* s, int K, long row, long col) {
-  uint8_t byte = w[row * (K / 2) + col / 2];
-  unsigned nib = (col & 1) ? (byte >> 4) : (byte & 15u);
-  return orc_e2m1(nib) * orc_e8m0(s[row * (K / 32) + col / 32]);
+/* Row `row` of a packed weight matrix with K elements per row, decoded into
+ * out[0..K): each element is its nibble's e2m1 value (even K index in the low
+ * half of the byte) times its 32-block's E8M0 scale (the product is exact). */
+static void decode_weight_row(const uint8_t* w, const uint8_t* s, int K, long row, double* out) {
+  double e2m1_of[16];
+  for (unsigned n = 0; n < 16; ++n) e2m1_of[n] = orc_e2m1(n);
+  for (int b = 0; b < K / 32; ++b) {
+    const double scale = orc_e8m0(s[row * (K / 32) + b]);
+    for (int c = 32 * b; c < 32 * b + 32; ++c) {
+      const uint8_t byte = w[row * (K / 2) + c / 2];
+      const unsigned nib = (c & 1) ? (byte >> 4) : (byte & 15u);
+      out[c] = e2m1_of[nib] * scale;
+    }
+  }
 }
 
 void orc_decode_fp4_matrix(const uint8_t* w, const uint8_t* s, long rows, int K, double* out) {
 #pragma omp parallel for schedule(static)
-  for (long r = 0; r < rows; ++r)
-    for (long c = 0; c < K; ++c) out[r * K + c] = weight_elem(w, s, K, r, c);
+  for (long r = 0; r < rows; ++r) decode_weight_row(w, s, K, r, out + r * K);
 }
 
 void orc_decode_mxfp8(const uint8_t* q, const uint8_t* s, long rows, int K, double* out) {
@@ -233,22 +240,6 @@ void orc_sort(const int32_t* ids, long P, int E, int32_t* counts, int32_t* offse
 
 /* ------------------------------------------------------------ expert FFN */
 
-/* Row `row` of a packed weight matrix with K elements per row, decoded into
- * out[0..K): each element is its nibble's e2m1 value (even K index in the low
- * half of the byte) times its 32-block's E8M0 scale (the product is exact). */
-static void decode_weight_row(const uint8_t* w, const uint8_t* s, int K, long row, acc_t* out) {
-  double e2m1_of[16];
-  for (unsigned n = 0; n < 16; ++n) e2m1_of[n] = orc_e2m1(n);
-  for (int b = 0; b < K / 32; ++b) {
-    const double scale = orc_e8m0(s[row * (K / 32) + b]);
-    for (int c = 32 * b; c < 32 * b + 32; ++c) {
-      const uint8_t byte = w[row * (K / 2) + c / 2];
-      const unsigned nib = (c & 1) ? (byte >> 4) : (byte & 15u);
-      out[c] = (acc_t)(e2m1_of[nib] * scale);
-    }
-  }
-}
-
 /* Gate/up projections of one MXFP8 activation row through expert weights
  * W1, W3 ([I, H] packed): G[i] = sum_h x[h] W1[i,h], U[i] likewise with W3,
  * summed in ascending h in acc_t (each product of an e4m3 and an e2m1 value
@@ -261,16 +252,16 @@ void orc_expert_gate_up(const uint8_t* xq, const uint8_t* xs, int H, int I,
   for (int h = 0; h < H; ++h) xd[h] = (acc_t)(orc_e4m3(xq[h]) * orc_e8m0(xs[h / 32]));
 #pragma omp parallel
   {
-    acc_t* r1 = (acc_t*)malloc(sizeof(acc_t) * (size_t)H);
-    acc_t* r3 = (acc_t*)malloc(sizeof(acc_t) * (size_t)H);
+    double* r1 = (double*)malloc(sizeof(double) * (size_t)H);
+    double* r3 = (double*)malloc(sizeof(double) * (size_t)H);
 #pragma omp for schedule(static)
     for (int i = 0; i < I; ++i) {
       decode_weight_row(w1, s1, H, i, r1);
       decode_weight_row(w3, s3, H, i, r3);
       acc_t g = 0, u = 0;
       for (int h = 0; h < H; ++h) {
-        g += xd[h] * r1[h];
-        u += xd[h] * r3[h];
+        g += xd[h] * (acc_t)r1[h];
+        u += xd[h] * (acc_t)r3[h];
       }
       G[i] = (double)g;
       U[i] = (double)u;
@@ -304,12 +295,12 @@ void orc_expert_down(const uint8_t* hq, const uint8_t* hs, int H, int I,
   for (int i = 0; i < I; ++i) hd[i] = (acc_t)(orc_e4m3(hq[i]) * orc_e8m0(hs[i / 32]));
 #pragma omp parallel
   {
-    acc_t* r2 = (acc_t*)malloc(sizeof(acc_t) * (size_t)I);
+    double* r2 = (double*)malloc(sizeof(double) * (size_t)I);
 #pragma omp for schedule(static)
     for (int r = 0; r < H; ++r) {
       decode_weight_row(w2, s2, I, r, r2);
       acc_t o = 0;
-      for (int i = 0; i < I; ++i) o += hd[i] * r2[i];
+      for (int i = 0; i < I; ++i) o += hd[i] * (acc_t)r2[i];
       O[r] = (double)o;
     }
     free(r2);
