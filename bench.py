@@ -420,7 +420,7 @@ def bench_shard(args):
         hq = torch.empty((P, Ig), dtype=torch.uint8, device=dev)
         hs = torch.empty((P, Ig // 32), dtype=torch.uint8, device=dev)
         O = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
-        sws = torch.empty(max(moe.stage_workspace_size(T, k, Eg, H, Ig), 256), dtype=torch.uint8, device=dev)
+        sws = torch.empty(max(moe.stage_workspace_size(T, Eg, k, H, Ig), 256), dtype=torch.uint8, device=dev)
 
         def step(i):
             pw = pws[i % copies]
@@ -430,7 +430,7 @@ def bench_shard(args):
         used = int((counts > 0).sum())
         rows = P
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
-        lws = torch.empty(max(moe.layer_workspace_size(T, k, Eg, H, Ig, args.flags), 256), dtype=torch.uint8,
+        lws = torch.empty(max(moe.layer_workspace_size(T, Eg, k, H, Ig, args.flags), 256), dtype=torch.uint8,
                           device=dev)
 
         def step(i):
@@ -591,16 +591,16 @@ def measure_layer(args, cfg: str, steps: int, warmup: int) -> dict:
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=dev)
     O = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
-    stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, kk, Ew, H, I), 256),
+    stage_ws = torch.empty(max(_lib.lib().moe_fp4_stage_workspace_size(T, Ew, kk, H, I), 256),
                            dtype=torch.uint8, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     ev_r = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(steps)]
     if args.full:
-        lws = torch.empty(max(moe.layer_full_workspace_size(T, k, Ew, H, I, ns, args.flags), 256),
+        lws = torch.empty(max(moe.layer_full_workspace_size(T, Ew, k, H, I, ns, args.flags), 256),
                           dtype=torch.uint8, device=dev)
     else:
-        lws = torch.empty(max(moe.layer_workspace_size(T, k, E, H, I, args.flags), 256),
+        lws = torch.empty(max(moe.layer_workspace_size(T, E, k, H, I, args.flags), 256),
                           dtype=torch.uint8, device=dev)
 
     def step(i):

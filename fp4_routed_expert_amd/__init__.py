@@ -140,12 +140,12 @@ def prepack_weights(w1, s1, w3, s3, w2, s2) -> PackedWeights:
     return PackedWeights(buffer=buf, desc=desc)
 
 
-def stage_workspace_size(T: int, k: int, E: int, H: int, I: int) -> int:
-    return int(_lib.lib().moe_fp4_stage_workspace_size(T, k, E, H, I))
+def stage_workspace_size(T: int, E: int, k: int, H: int, I: int) -> int:
+    return int(_lib.lib().moe_fp4_stage_workspace_size(T, E, k, H, I))
 
 
 def _stage_ws(T, k, pw, dev, workspace):
-    need = stage_workspace_size(T, k, pw.E, pw.H, pw.I)
+    need = stage_workspace_size(T, pw.E, k, pw.H, pw.I)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     return workspace
@@ -191,8 +191,8 @@ def combine(O, gates, pair_pos, T: int, k: int, H: int, y=None):
     return y
 
 
-def forward_workspace_size(T: int, k: int, E: int, H: int, I: int, flags: int = 0) -> int:
-    return int(_lib.lib().moe_fp4_forward_workspace_size(T, k, E, H, I, flags))
+def forward_workspace_size(T: int, E: int, k: int, H: int, I: int, flags: int = 0) -> int:
+    return int(_lib.lib().moe_fp4_forward_workspace_size(T, E, k, H, I, flags))
 
 
 def grouped_forward(pw: PackedWeights, xq, xs, gates, offsets, sorted_pair, pair_pos, flags: int = 0,
@@ -203,7 +203,7 @@ def grouped_forward(pw: PackedWeights, xq, xs, gates, offsets, sorted_pair, pair
     if y is None:
         y = torch.empty((T, pw.H), dtype=torch.float32, device=dev)
     if workspace is None:
-        need = forward_workspace_size(T, k, pw.E, pw.H, pw.I, flags)
+        need = forward_workspace_size(T, pw.E, k, pw.H, pw.I, flags)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _lib.check(_lib.lib().moe_fp4_grouped_forward(
         ctypes.byref(pw.desc), _ptr(xq), _ptr(xs), _ptr(gates), _ptr(offsets), _ptr(sorted_pair),
@@ -212,8 +212,8 @@ def grouped_forward(pw: PackedWeights, xq, xs, gates, offsets, sorted_pair, pair
     return y
 
 
-def layer_workspace_size(T: int, k: int, E: int, H: int, I: int, flags: int = 0) -> int:
-    return int(_lib.lib().moe_fp4_layer_workspace_size(T, k, E, H, I, flags))
+def layer_workspace_size(T: int, E: int, k: int, H: int, I: int, flags: int = 0) -> int:
+    return int(_lib.lib().moe_fp4_layer_workspace_size(T, E, k, H, I, flags))
 
 
 def layer_forward(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: int, flags: int = 0,
@@ -229,7 +229,7 @@ def layer_forward(pw: PackedWeights, x: torch.Tensor, logits: torch.Tensor, k: i
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
     if workspace is None:
-        need = layer_workspace_size(T, k, pw.E, pw.H, pw.I, flags)
+        need = layer_workspace_size(T, pw.E, k, pw.H, pw.I, flags)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _lib.check(_lib.lib().moe_fp4_layer_forward(
         ctypes.byref(pw.desc), _ptr(x), _ptr(logits), T, k, _ptr(y), _ptr(workspace),
@@ -321,9 +321,9 @@ def combine_shared(O, gates, pair_pos, O_shared, T: int, k: int, H: int, y=None)
     return y
 
 
-def layer_full_workspace_size(T: int, k: int, E: int, H: int, I: int, n_shared: int = 0,
+def layer_full_workspace_size(T: int, E: int, k: int, H: int, I: int, n_shared: int = 0,
                               flags: int = 0) -> int:
-    return int(_lib.lib().moe_fp4_layer_full_workspace_size(T, k, E, H, I, n_shared, flags))
+    return int(_lib.lib().moe_fp4_layer_full_workspace_size(T, E, k, H, I, n_shared, flags))
 
 
 def layer_forward_full(pw: PackedWeights, n_shared: int, router_w: torch.Tensor, x: torch.Tensor,
@@ -340,7 +340,7 @@ def layer_forward_full(pw: PackedWeights, n_shared: int, router_w: torch.Tensor,
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
     if workspace is None:
-        need = layer_full_workspace_size(T, k, pw.E, pw.H, pw.I, n_shared, flags)
+        need = layer_full_workspace_size(T, pw.E, k, pw.H, pw.I, n_shared, flags)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _lib.check(_lib.lib().moe_fp4_layer_forward_full(
         ctypes.byref(pw.desc), n_shared, _ptr(router_w), _ptr(x), T, k, _ptr(y), _ptr(workspace),

@@ -18,7 +18,8 @@
 //
 // Decode (few tokens): weight streaming.  A workgroup owns one 32-row group
 // (two tiles, so each activation fragment serves two MFMAs) and one 16-token
-// tile; its 16 waves take the K-steps in turn (wave w: steps w, w + 16, ...),
+// tile, or two from 17 tokens (each weight tile then feeds the MFMAs of both
+// token tiles); its 16 waves take the K-steps in turn (wave w: steps w, w + 16, ...),
 // so at any moment they read neighbouring 4 KiB blocks, each keeping two steps
 // in flight; partial sums meet in LDS in wave order.  Prefill: LDS-tiled
 // GEMM, 128 tokens x 128 rows per workgroup, 128 K per stage, two register

@@ -6,37 +6,16 @@
 // splitting K; each wave issues 128-bit loads of whole 1 KiB tiles (a tile is
 // contiguous in the packed layout, so a wave's load is one 1 KiB run) plus one
 // word per lane per K-step holding the tiles' E8M0 scales.  A wave's K-steps
-// are taken in batches of kB whose loads are issued back to back; with
-// pipelining on, the loads of the next batch are in flight while the current
-// one is multiplied, so each wave keeps one to two batches of weight bytes
-// outstanding all the time.  The dot products run on the gfx950 scaled MFMA
+// are taken in batches of kB whose loads are issued back to back, so each wave
+// keeps a batch of weight bytes outstanding.  The dot products run on the gfx950 scaled MFMA
 // (v_mfma_scale_f32_16x16x128_f8f6f4, MXFP8 activations as A, FP4 weights as
 // B, one E8M0 scale per lane and operand), which applies the block scales in
 // hardware: the token rows are padded to 16, compute is far below the
 // roofline here.  The waves' partial sums are added in a fixed order through
 // LDS (no atomics: pwwt.cn review, section 4.2), then wave 0 runs the epilogue
-// -- SwiGLU and MXFP8 requantisation of h for the gate/up kernel, the fp32
-// store of O for the down kernel.
+// -- SwiGLU and MXFP8 requantisation of h for the gate/up kernel, the bf16
+// (round to nearest even) store of O for the down kernel.
 #include "common.h"
-
-#ifndef DEC_UP_NW
-#define DEC_UP_NW 4
-#endif
-#ifndef DEC_UP_B
-#define DEC_UP_B 4
-#endif
-#ifndef DEC_UP_PIPE
-#define DEC_UP_PIPE 0
-#endif
-#ifndef DEC_DN_NW
-#define DEC_DN_NW 2
-#endif
-#ifndef DEC_DN_B
-#define DEC_DN_B 6
-#endif
-#ifndef DEC_DN_PIPE
-#define DEC_DN_PIPE 0
-#endif
 
 namespace moe {
 namespace {
@@ -139,31 +118,23 @@ __device__ __forceinline__ void mma_batch(const Step<NT, NG> (&r)[kB], v4f* acc,
     if (j + u < j1) mma_step<NT, NG>(r[u], acc);
 }
 
-// Multiply-accumulate K-steps [j0, j1) of one wave into acc.
-template <int NT, int NG, int kB, bool kPipe>
+// Multiply-accumulate K-steps [j0, j1) of one wave into acc, kB steps' loads
+// issued back to back before their MFMAs.
+template <int NT, int NG, int kB>
 __device__ __forceinline__ void stream_k(const Stream<NT, NG>& st, int j0, int j1, v4f* acc) {
-  if constexpr (!kPipe) {
-    for (int j = j0; j < j1; j += kB) {
-      Step<NT, NG> r[kB];
-      load_batch<NT, NG, kB>(r, st, j, j1);
-      mma_batch<NT, NG, kB>(r, acc, j, j1);
-    }
-  } else {
-    // two register sets taken in turn, so no loaded register is ever copied
-    Step<NT, NG> x[kB], y[kB];
-    if (j0 < j1) load_batch<NT, NG, kB>(x, st, j0, j1);
-    for (int j = j0; j < j1; j += 2 * kB) {
-      if (j + kB < j1) load_batch<NT, NG, kB>(y, st, j + kB, j1);
-      mma_batch<NT, NG, kB>(x, acc, j, j1);
-      if (j + kB >= j1) break;
-      if (j + 2 * kB < j1) load_batch<NT, NG, kB>(x, st, j + 2 * kB, j1);
-      mma_batch<NT, NG, kB>(y, acc, j + kB, j1);
-    }
+  for (int j = j0; j < j1; j += kB) {
+    Step<NT, NG> r[kB];
+    load_batch<NT, NG, kB>(r, st, j, j1);
+    mma_batch<NT, NG, kB>(r, acc, j, j1);
   }
 }
 
-constexpr int kUpNW = DEC_UP_NW;
-constexpr int kDnNW = DEC_DN_NW;
+// Waves per workgroup and K-steps per load batch (one row group per pass;
+// halved, rounded up, with two): measured over 2-8 waves and batches of 2-8.
+constexpr int kUpNW = 4;
+constexpr int kUpB = 4;
+constexpr int kDnNW = 2;
+constexpr int kDnB = 6;
 
 // NG row groups of 16 per pass over the weights: NG = 1 for a handful of rows
 // per expert, NG = 2 when the expected rows per expert fill more than one
@@ -200,7 +171,7 @@ __global__ __launch_bounds__(kUpNW * 64) void up_decode_kernel(
     for (int t = 0; t < NG * 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
     // two row groups double the activation registers of a K-step: half the
     // K-steps per batch keeps the kernel within its registers
-    stream_k<4, NG, NG == 2 ? (DEC_UP_B + 1) / 2 : DEC_UP_B, DEC_UP_PIPE != 0>(st, j0, j1, acc);
+    stream_k<4, NG, NG == 2 ? (kUpB + 1) / 2 : kUpB>(st, j0, j1, acc);
 #pragma unroll
     for (int t = 0; t < NG * 4; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
@@ -266,7 +237,7 @@ __global__ __launch_bounds__(kDnNW * 64) void down_decode_kernel(
     v4f acc[NG * 2];
 #pragma unroll
     for (int t = 0; t < NG * 2; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    stream_k<2, NG, NG == 2 ? (DEC_DN_B + 1) / 2 : DEC_DN_B, DEC_DN_PIPE != 0>(st, j0, j1, acc);
+    stream_k<2, NG, NG == 2 ? (kDnB + 1) / 2 : kDnB>(st, j0, j1, acc);
 #pragma unroll
     for (int t = 0; t < NG * 2; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();

@@ -12,10 +12,10 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+// Every launch records its result for moe_last_hip_error (0 on success).
 moe_status_t hip_status(hipError_t e) {
-  if (e == hipSuccess) return MOE_OK;
   g_last_hip_error = (int)e;
-  return MOE_ERR_HIP;
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -268,7 +268,7 @@ moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1, const
   return MOE_OK;
 }
 
-size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+size_t moe_fp4_stage_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
   if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
   return stage_ws_bytes(T, k, E, H, I);
 }
@@ -333,7 +333,7 @@ moe_status_t moe_combine(const uint16_t* O, const float* topk_gates, const int32
   return hip_status(launch_combine(O, topk_gates, pair_pos, nullptr, T, k, H, y, stream));
 }
 
-size_t moe_fp4_forward_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+size_t moe_fp4_forward_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
                                       uint32_t flags) {
   (void)flags;
   if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
@@ -376,7 +376,7 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w, const uint8_t* 
 
 extern "C" {
 
-size_t moe_fp4_layer_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+size_t moe_fp4_layer_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
                                     uint32_t flags) {
   (void)flags;
   if (check_tek(T, E, k) != MOE_OK || check_hi(H, I) != MOE_OK) return 0;
@@ -555,7 +555,7 @@ static moe_status_t check_full(int32_t T, int32_t k, int32_t E, int32_t H, int32
   return check_router(T, H, E - ns);
 }
 
-size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
                                          int32_t n_shared, uint32_t flags) {
   (void)flags;
   if (E < 1 || E > kMaxE || check_hi(H, I) != MOE_OK) return 0;

@@ -29,10 +29,11 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ v8bf as_bf8(uint4 v) { return __builtin_bit_cast(v8bf, v); }
 
-// Chunks of 32 K in flight per wave (a chunk is TM + 4 16-byte loads per lane).
+// Chunks of 32 K in flight per wave (a chunk is TM + 4 16-byte loads per lane),
+// for either token-tile count.
 template <int TM>
 constexpr int ring_depth() {
-  return TM == 1 ? 3 : 3;
+  return 3;
 }
 
 template <int TM>

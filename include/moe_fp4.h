@@ -39,6 +39,9 @@
  *  - Determinism: the same inputs give bitwise-identical outputs, run to run.
  *    No floating-point atomics anywhere; reductions go in a fixed order
  *    (pwwt.cn review, section 4.2).
+ *  - Size queries take (T, E, k, H, I, ...) in that order, like
+ *    moe_sort_permute_workspace_size; the compute calls take their own
+ *    argument lists as declared.
  *  - Supported shapes: 1 <= k <= min(E, 32), E <= 1024, H % 128 == 0,
  *    I % 128 == 0, 0 <= T, T*k < 2^31.  T == 0 is a no-op.  Anything else
  *    returns MOE_ERR_UNSUPPORTED (or MOE_ERR_INVALID_ARGUMENT for negative
@@ -67,7 +70,11 @@ typedef enum moe_status {
 /* Static string naming a status code (never NULL). */
 const char* moe_status_string(moe_status_t status);
 
-/* The hipError_t of the last failed launch on the calling thread (0 if none). */
+/* The hipError_t of the calling thread's most recent HIP operation through
+ * this library (a kernel launch, or the scratch lookup of the no-allocation
+ * entry point): 0 when it succeeded or when the thread has made none (a call
+ * rejected by the argument checks makes none and leaves the value as it was).
+ * Read it after a call returned MOE_ERR_HIP. */
 int moe_last_hip_error(void);
 
 /* Layout version of moe_fp4_prepack_weights' output. */
@@ -169,11 +176,11 @@ moe_status_t moe_fp4_prepack_weights(const uint8_t* w1, const uint8_t* s1,
  *   on are neither computed nor written, but sorted_pair keeps T*k entries,
  *   each a valid pair index.  The same holds for moe_fp4_expert_down.
  *   The prefill path needs T*H < 2^32 (MOE_ERR_UNSUPPORTED otherwise).
- *   workspace >= moe_fp4_stage_workspace_size(T, k, E, H, I), 256-aligned
+ *   workspace >= moe_fp4_stage_workspace_size(T, E, k, H, I), 256-aligned
  *   (the prefill path's tile list and its activation scales rearranged by
  *   K-step; contents on entry are ignored)
  */
-size_t moe_fp4_stage_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I);
+size_t moe_fp4_stage_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
 moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w /*(host)*/,
                                const uint8_t* xq, const uint8_t* xs,
                                const int32_t* expert_offsets, const int32_t* sorted_pair,
@@ -208,10 +215,10 @@ moe_status_t moe_combine(const uint16_t* O, const float* topk_gates, const int32
 /*
  * Steps 4-7 in one call: expert_up -> expert_down -> combine, with hq, hs, O
  * and the tile map held in `workspace`
- * (>= moe_fp4_forward_workspace_size(T, k, E, H, I, flags) bytes, 256-aligned).
+ * (>= moe_fp4_forward_workspace_size(T, E, k, H, I, flags) bytes, 256-aligned).
  *   y [T, H] fp32 (out, overwritten)
  */
-size_t moe_fp4_forward_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+size_t moe_fp4_forward_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
                                       uint32_t flags);
 moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w /*(host)*/,
                                      const uint8_t* xq, const uint8_t* xs, const float* topk_gates,
@@ -227,13 +234,13 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w /*(host)*/,
  * T <= 16 the three front steps run as one fused launch (routing and sort in
  * one workgroup, quantisation in the others); larger T uses the stand-alone
  * kernels.  Every intermediate lives in `workspace`
- * (>= moe_fp4_layer_workspace_size(T, k, E, H, I, flags) bytes, 256-aligned;
+ * (>= moe_fp4_layer_workspace_size(T, E, k, H, I, flags) bytes, 256-aligned;
  * contents on entry are ignored, on exit unspecified).
  *   x_bf16 [T, H] bf16 bits (16-byte aligned); logits [T, E] fp32
  *   y [T, H] fp32 (out, overwritten, 16-byte aligned)
  *   flags: MOE_FLAG_FORCE_DECODE / MOE_FLAG_FORCE_PREFILL as above
  */
-size_t moe_fp4_layer_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+size_t moe_fp4_layer_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
                                     uint32_t flags);
 moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w /*(host)*/,
                                    const uint16_t* x_bf16, const float* logits,
@@ -250,7 +257,7 @@ moe_status_t moe_fp4_layer_forward(const moe_fp4_weights_t* w /*(host)*/,
  * first call on a device).  The call allocates, frees and clears nothing; the
  * caller passes inputs and outputs only.  Results are bitwise those of
  * moe_fp4_layer_forward on the same inputs.
- *  - Shapes whose moe_fp4_layer_workspace_size(T, k, E, H, I, flags) exceeds
+ *  - Shapes whose moe_fp4_layer_workspace_size(T, E, k, H, I, flags) exceeds
  *    MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE, nothing enqueued
  *    (64 MiB holds T <= 476 at H7168 I2048 E256 top-8, T <= 1052 at H4096
  *    I1536 E64 top-6).
@@ -334,11 +341,11 @@ moe_status_t moe_combine_shared(const uint16_t* O, const float* topk_gates, cons
  *   w: E = E_routed + n_shared experts (0 <= n_shared < E); router_w
  *   [E_routed, H] bf16 bits; x_bf16 [T, H] bf16 bits; y [T, H] fp32 (out)
  *   1 <= k <= E_routed, k + n_shared <= 32
- *   workspace >= moe_fp4_layer_full_workspace_size(T, k, E, H, I, n_shared,
+ *   workspace >= moe_fp4_layer_full_workspace_size(T, E, k, H, I, n_shared,
  *   flags) bytes, 256-aligned
  *   flags: MOE_FLAG_FORCE_DECODE / MOE_FLAG_FORCE_PREFILL as above
  */
-size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+size_t moe_fp4_layer_full_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I,
                                          int32_t n_shared, uint32_t flags);
 moe_status_t moe_fp4_layer_forward_full(const moe_fp4_weights_t* w /*(host)*/, int32_t n_shared,
                                         const uint16_t* router_w, const uint16_t* x_bf16,

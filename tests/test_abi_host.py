@@ -100,7 +100,7 @@ def _desc(E=8, H=256, I=128, version=1):
 
 def test_forward_argument_errors():
     d = _desc()
-    ws = L.moe_fp4_forward_workspace_size(16, 2, 8, 256, 128, 0)
+    ws = L.moe_fp4_forward_workspace_size(16, 8, 2, 256, 128, 0)
     assert ws >= 32 * 128 + 32 * 4 + 32 * 256 * 2   # hq, hs and the bf16 expert outputs O
     fwd = L.moe_fp4_grouped_forward
     assert fwd(ctypes.byref(_desc(version=7)), A, A, A, A, A, A, 16, 2, A, A, ws, 0, NUL) == INV
@@ -113,12 +113,12 @@ def test_forward_argument_errors():
     small.packed_bytes -= 1
     assert fwd(ctypes.byref(small), A, A, A, A, A, A, 16, 2, A, A, ws, 0, NUL) == INV
     up = L.moe_fp4_expert_up
-    sws = L.moe_fp4_stage_workspace_size(16, 2, 8, 256, 128)
+    sws = L.moe_fp4_stage_workspace_size(16, 8, 2, 256, 128)
     assert sws >= 32 * (256 // 128) * 4          # the activation scales by K-step
-    assert L.moe_fp4_stage_workspace_size(16, 2, 8, 200, 128) == 0
+    assert L.moe_fp4_stage_workspace_size(16, 8, 2, 200, 128) == 0
     assert up(ctypes.byref(d), A, A, A, A, 16, 2, A, A, A, sws - 1, 0, NUL) == WSE
     big = _desc(E=8, H=1 << 20, I=128)
-    bws = L.moe_fp4_stage_workspace_size(4096, 2, 8, 1 << 20, 128)
+    bws = L.moe_fp4_stage_workspace_size(4096, 8, 2, 1 << 20, 128)
     assert up(ctypes.byref(big), A, A, A, A, 4096, 2, A, A, A, bws, 2, NUL) == UNS  # T*H >= 2^32, prefill
     assert L.moe_combine(A, A, A, 4, 2, 250, A, NUL) == UNS       # H % 4
     assert L.moe_combine(A, A, A, 4, 0, 256, A, NUL) == INV
@@ -126,10 +126,10 @@ def test_forward_argument_errors():
 
 def test_layer_forward_argument_errors():
     d = _desc()
-    need = L.moe_fp4_layer_workspace_size(16, 2, 8, 256, 128, 0)
+    need = L.moe_fp4_layer_workspace_size(16, 8, 2, 256, 128, 0)
     # holds at least the forward workspace plus ids, gates, sort arrays and MXFP8 x
-    assert need >= L.moe_fp4_forward_workspace_size(16, 2, 8, 256, 128, 0) + 16 * 256
-    assert L.moe_fp4_layer_workspace_size(16, 9, 8, 256, 128, 0) == 0   # k > E
+    assert need >= L.moe_fp4_forward_workspace_size(16, 8, 2, 256, 128, 0) + 16 * 256
+    assert L.moe_fp4_layer_workspace_size(16, 8, 9, 256, 128, 0) == 0   # k > E
     lf = L.moe_fp4_layer_forward
     assert lf(ctypes.byref(d), A, A, 16, 2, A, A, need - 1, 0, NUL) == WSE
     assert lf(ctypes.byref(d), A, A, 16, 2, A, NUL, need, 0, NUL) == WSE
@@ -177,15 +177,15 @@ def test_router_and_shared_argument_errors():
     assert cs(A, A, A, A, 4, 2, 256, MIS, NUL) == INV                        # y not 16-aligned
     d = _desc()                    # 8 experts
     full = L.moe_fp4_layer_full_workspace_size
-    n0 = full(16, 2, 8, 256, 128, 0, 0)
-    n1 = full(16, 2, 8, 256, 128, 1, 0)   # 7 routed + 1 shared: 3 slots per token
-    assert n0 >= (L.moe_fp4_layer_workspace_size(16, 2, 8, 256, 128, 0)
+    n0 = full(16, 8, 2, 256, 128, 0, 0)
+    n1 = full(16, 8, 2, 256, 128, 1, 0)   # 7 routed + 1 shared: 3 slots per token
+    assert n0 >= (L.moe_fp4_layer_workspace_size(16, 8, 2, 256, 128, 0)
                   + L.moe_router_workspace_size(16, 256, 8))                  # + router planes
-    assert n1 >= L.moe_fp4_layer_workspace_size(16, 3, 8, 256, 128, 0)
-    assert full(16, 2, 8, 256, 128, 8, 0) == 0          # no routed expert left
-    assert full(16, 2, 8, 256, 128, -1, 0) == 0
+    assert n1 >= L.moe_fp4_layer_workspace_size(16, 8, 3, 256, 128, 0)
+    assert full(16, 8, 2, 256, 128, 8, 0) == 0          # no routed expert left
+    assert full(16, 8, 2, 256, 128, -1, 0) == 0
     assert full(16, 8, 8, 256, 128, 1, 0) == 0          # k > routed experts
-    assert full(16, 30, 64, 256, 128, 3, 0) == 0        # k + n_shared > 32
+    assert full(16, 64, 30, 256, 128, 3, 0) == 0        # k + n_shared > 32
     lf = L.moe_fp4_layer_forward_full
     assert lf(ctypes.byref(d), 0, A, A, 16, 2, A, A, n0 - 1, 0, NUL) == WSE
     assert n1 > n0
@@ -250,5 +250,18 @@ def test_noalloc_argument_errors():
     assert f(wp, A, A, 8, 8, A, 3, NUL) == INV                  # both paths forced
     assert f(wp, A, A, 8, 300, A, 0, NUL) == UNS                # k > 32
     assert f(wp, A, A, 0, 8, NUL, 0, NUL) == 0                  # T = 0: no-op
-    assert L.moe_fp4_layer_workspace_size(477, 8, 256, 7168, 2048, 0) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_fp4_layer_workspace_size(477, 256, 8, 7168, 2048, 0) > _lib.MOE_NOALLOC_SCRATCH_BYTES
     assert f(wp, A, A, 477, 8, A, 0, NUL) == WSE                # beyond the fixed scratch
+
+
+def test_size_queries_take_t_e_k_order():
+    """Every size query takes (T, E, k, ...), like moe_sort_permute_workspace_size:
+    swapping E and k changes the answer (or makes the shape invalid)."""
+    T, E, k, H, I = 64, 32, 4, 256, 128
+    for f, extra in ((L.moe_fp4_stage_workspace_size, ()), (L.moe_fp4_forward_workspace_size, (0,)),
+                     (L.moe_fp4_layer_workspace_size, (0,))):
+        assert f(T, E, k, H, I, *extra) > 0
+        assert f(T, k, E, H, I, *extra) == 0           # k = 32 > E = 4
+    full = L.moe_fp4_layer_full_workspace_size
+    assert full(T, E, k, H, I, 1, 0) > 0 and full(T, k, E, H, I, 1, 0) == 0
+    assert L.moe_fp4_layer_workspace_size(T, E, k, H, I, 0) > L.moe_fp4_layer_workspace_size(T, E, 2, H, I, 0)

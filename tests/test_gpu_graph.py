@@ -34,7 +34,7 @@ def test_layer_graph_replays_match_eager(shape, flags, dev):
     x_buf = c.x.clone()
     l_buf = c.logits.clone()
     y = torch.empty((sh.T, sh.H), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(moe.layer_workspace_size(sh.T, sh.k, sh.E, sh.H, sh.I, flags), 256),
+    ws = torch.empty(max(moe.layer_workspace_size(sh.T, sh.E, sh.k, sh.H, sh.I, flags), 256),
                      dtype=torch.uint8, device=dev)
     moe.layer_forward(c.pw, x_buf, l_buf, sh.k, flags, y=y, workspace=ws)  # warm-up outside capture
     torch.cuda.synchronize()
@@ -81,7 +81,7 @@ def test_full_layer_and_dense_graph_replays_match_eager(dev):
     yd = torch.empty((sh.T, 96), dtype=torch.bfloat16, device=dev)
     xq = torch.empty((sh.T, sh.H), dtype=torch.uint8, device=dev)
     xs = torch.empty((sh.T, sh.H // 32), dtype=torch.uint8, device=dev)
-    ws = torch.empty(moe.layer_full_workspace_size(sh.T, sh.k, sh.E + 1, sh.H, sh.I, 1),
+    ws = torch.empty(moe.layer_full_workspace_size(sh.T, sh.E + 1, sh.k, sh.H, sh.I, 1),
                      dtype=torch.uint8, device=dev)
 
     def run():

@@ -72,7 +72,7 @@ def test_layer_forward_poisoned_workspace(dev):
     c = get_case("c1", dev)
     T, k, E, H, I = c.sh.T, c.sh.k, c.sh.E, c.sh.H, c.sh.I
     y_ref = moe.layer_forward(c.pw, c.x, c.logits, k)
-    need = moe.layer_workspace_size(T, k, E, H, I)
+    need = moe.layer_workspace_size(T, E, k, H, I)
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
     y = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
     moe.layer_forward(c.pw, c.x, c.logits, k, y=y, workspace=ws)

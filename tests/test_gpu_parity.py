@@ -195,7 +195,7 @@ def test_poisoned_workspace_and_outputs(path, dev):
     c = get_case("c0", dev)
     T, k, E, H, I = c.sh.T, c.sh.k, c.sh.E, c.sh.H, c.sh.I
     y_ref, it = _run_layer(c, PATHS[path])
-    need = moe.forward_workspace_size(T, k, E, H, I)
+    need = moe.forward_workspace_size(T, E, k, H, I)
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
     y = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
     moe.grouped_forward(c.pw, it["xq"], it["xs"], it["topk_gates"], it["expert_offsets"],

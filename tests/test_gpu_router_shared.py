@@ -235,7 +235,7 @@ def test_layer_full_repeatable_and_workspace_poison(dev):
     sh = c.sh
     wg = _bf16_dev(synth.make_router_weights(sh), dev)
     pw = _with_shared(c, _shared_list(sh, 1), dev)
-    need = moe.layer_full_workspace_size(sh.T, sh.k, sh.E + 1, sh.H, sh.I, 1)
+    need = moe.layer_full_workspace_size(sh.T, sh.E + 1, sh.k, sh.H, sh.I, 1)
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev)
     y1 = moe.layer_forward_full(pw, 1, wg, c.x, sh.k, workspace=ws)
     ws.fill_(0x3C)

@@ -44,7 +44,7 @@ def test_noalloc_rejects_shapes_beyond_the_scratch(dev):
     c = get_case("c2", dev)
     k, H, E, I = c.sh.k, c.sh.H, c.sh.E, c.sh.I
     T = 4096                                  # its layer workspace is far beyond 64 MiB
-    assert moe.layer_workspace_size(T, k, E, H, I) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert moe.layer_workspace_size(T, E, k, H, I) > _lib.MOE_NOALLOC_SCRATCH_BYTES
     x = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
     lg = torch.zeros((T, E), dtype=torch.float32, device=dev)
     y = torch.full((T, H), 7.0, dtype=torch.float32, device=dev)
