@@ -58,6 +58,27 @@ def build(verbose: bool = False) -> str:
     return SO
 
 
+# Stand-alone GPU check programs of the test suite (built here, on the CPU,
+# so that the GPU tests only run them).
+CHECKS = {
+    os.path.join(ROOT, "tests", "native", "cvt_equivalence.hip"):
+        os.path.join(ROOT, "tests", "native", "_build", "cvt_equivalence"),
+}
+
+
+def build_checks(verbose: bool = False) -> None:
+    for src, exe in CHECKS.items():
+        os.makedirs(os.path.dirname(exe), exist_ok=True)
+        flags = [f for f in HIP_FLAGS if f not in ("-fPIC",)]
+        cmd = [HIPCC, *flags, "-I", CSRC, src, "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        if verbose:
+            print("built", exe)
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_checks(verbose=True)
     sys.exit(0)

@@ -51,10 +51,29 @@ __host__ __device__ __forceinline__ uint32_t f32_to_e4m3(float a) {
   return sign | c;
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// The same codes from the gfx950 conversion instruction (v_cvt_pk_fp8_f32:
+// OCP e4m3fn, round to nearest even) after a clamp to +-448, which makes the
+// overflow saturate as above; equal to f32_to_e4m3 for every |a| < 512
+// (tests/native/cvt_equivalence.hip checks each of those inputs).  Two
+// values give bytes 0 and 1; four give a whole dword, a in byte 0.
+__device__ __forceinline__ float e4m3_clamp(float a) { return __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f); }
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs): the gfx950
+// conversion instruction (v_cvt_pk_bf16_f32), equal for every finite input
+// to rounding the bit pattern, (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+// (tests/native/cvt_equivalence.hip checks each of them).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t f32x2_to_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // SiLU(g) * u with the hardware exponential and reciprocal (fp32, about one

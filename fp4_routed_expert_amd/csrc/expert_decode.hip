@@ -198,8 +198,9 @@ __global__ __launch_bounds__(kUpNW * 64) void up_decode_kernel(
           const int r = m0 + 16 * g + 4 * (lane >> 4) + v;
           if (r < seg1) {
             uint8_t* hrow = hq + (size_t)r * I + q * 32 + (lane & 15);
-            hrow[0] = (uint8_t)f32_to_e4m3(h0 * mul);
-            hrow[16] = (uint8_t)f32_to_e4m3(h1 * mul);
+            const uint32_t c2 = f32x2_to_e4m3(h0 * mul, h1 * mul);
+            hrow[0] = (uint8_t)c2;
+            hrow[16] = (uint8_t)(c2 >> 8);
             if ((lane & 15) == 0) hs[(size_t)r * (I / 32) + q] = (uint8_t)sc;
           }
         }

@@ -532,8 +532,9 @@ __device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int b
         const int r = rbase + v;
         if (r < cur.rows) {
           auto* hrow = hq + (size_t)(cur.m0 + r) * I + q * 32 + (lane & 15);
-          hrow[0] = (uint8_t)f32_to_e4m3(h0 * mul);
-          hrow[16] = (uint8_t)f32_to_e4m3(h1 * mul);
+          const uint32_t c2 = f32x2_to_e4m3(h0 * mul, h1 * mul);
+          hrow[0] = (uint8_t)c2;
+          hrow[16] = (uint8_t)(c2 >> 8);
           if ((lane & 15) == 0) hs[(size_t)(cur.m0 + r) * (I / 32) + q] = (uint8_t)sc;
         }
       }

@@ -234,11 +234,8 @@ __device__ __forceinline__ void quant_group8(const uint4* __restrict__ x, long i
   amax = quad_max(amax);
   float mul;
   const uint32_t scode = mx_scale_from_amax(amax, &mul);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(v[e] * mul) << (8 * e);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(v[4 + e] * mul) << (8 * e);
+  const uint32_t lo = f32x4_to_e4m3(v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul);
+  const uint32_t hi = f32x4_to_e4m3(v[4] * mul, v[5] * mul, v[6] * mul, v[7] * mul);
   if (live) {
     q[i] = make_uint2(lo, hi);
     if ((i & 3) == 0) sc[i >> 2] = (uint8_t)scode;
