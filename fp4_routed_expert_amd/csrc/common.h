@@ -89,6 +89,16 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
 
+// Maximum over lanes l, l^16, l^32, l^48 (the same lane of the wave's four
+// rows of 16), returned to all four: the gfx950 row swaps (v_permlane32_swap
+// pairs lane l with l^32, v_permlane16_swap pairs l with l^16), no LDS.
+__device__ __forceinline__ float max_lanes_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Maximum over each quad of 4 lanes, returned to every lane of the quad.
 __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));  // quad_perm [1,0,3,2]

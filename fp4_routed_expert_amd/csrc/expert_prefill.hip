@@ -85,16 +85,13 @@ static_assert(sizeof(Stage) % 16 == 0, "stage alignment");
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// The FP4 B operand occupies the low 4 registers of the 8-register operand;
+// An FP4 operand occupies the low 4 registers of the 8-register operand;
 // the upper half is left undefined so no registers are spent on it.
 __device__ __forceinline__ v8i widen_fp4(uint4 b) {
   const v4i v = v4i{(int)b.x, (int)b.y, (int)b.z, (int)b.w};
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
-__device__ __forceinline__ v4f mfma_fp8_fp4(v8i a, v8i b, v4f c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
-}
 
 // Byte offset of 16-byte chunk c (0..7) of activation row r in a stage.
 __device__ __forceinline__ int a_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
@@ -301,13 +298,24 @@ __device__ __forceinline__ void read_tail(Tail<N>& f, const uint8_t* S, const Ld
     read_a(f.a[i], f.sa[i], S, o, FragsShape<N>::kHead + i);
 }
 
-// Weight tile t's scale: byte t of the up dword, byte t&1 of the down pair
-// of q2-group t>>1 -- selected by the MFMA's scale operand byte select.
+// One 16x16 block of the product.  Gate/up computes the transposed block:
+// the weight tile is the MFMA's A operand (FP4, 16 features x 128 K) and the
+// activation fragment its B operand (FP8, 128 K x 16 tokens) -- the two
+// operands' lane layouts are the same (lane l: row or column l%16, K block
+// l/16), so a fragment serves either way round -- and the result holds
+// features 4(l/16)..4(l/16)+3 of token l%16 in lane l, so the epilogue
+// writes each token's 4 fp8 codes as one dword.  Down keeps activations as A:
+// lane l holds tokens 4(l/16)..+3 of feature l%16, and its bf16 stores of 16
+// lanes fill 32 bytes of 4 rows -- measured faster than 8-byte stores that
+// touch 16 rows each.  Weight tile t's scale: byte t of the up dword, byte
+// t&1 of the down pair of q2-group t>>1 -- selected by the MFMA's scale
+// operand byte select.
 template <bool kUp, int T>
 __device__ __forceinline__ v4f mfma_t(v8i a, uint32_t sa, uint4 b, const uint32_t* sb, v4f c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, widen_fp4(b), c, 0, 4, 0, (int)sa,
-                                                          kUp ? T : (T & 1),
-                                                          (int)(kUp ? sb[0] : sb[T >> 1]));
+  if (kUp)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen_fp4(b), a, c, 4, 0, T, (int)sb[0], 0, (int)sa);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, widen_fp4(b), c, 0, 4, 0, (int)sa, T & 1,
+                                                          (int)sb[T >> 1]);
 }
 
 template <bool kUp, int N>
@@ -516,34 +524,43 @@ __device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int b
   auto* __restrict__ hq = as_global(ka.hq);
   auto* __restrict__ hs = as_global(ka.hs);
   auto* __restrict__ O = as_global(ka.O);
-  // lane holds rows 4*(lane>>4)+v of each 16-row sub-tile, column lane&15 of each tile
+  const int g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const int rbase = 16 * (wm + 2 * i) + 4 * (lane >> 4);
     if (kUp) {
-      const int q = 4 * cur.ft + wn;  // 32-feature group of I
+      // lane holds token row 16 (wm + 2i) + lane%16 and h features 4g + v
+      // (tiles 0 and 2: W1 and W3 rows 0-15) and 16 + 4g + v (tiles 1 and 3)
+      // of q-group q, v < 4; one E8M0 scale per token over its 32 features,
+      // which lie in lanes l, l^16, l^32, l^48
+      const int r = 16 * (wm + 2 * i) + (lane & 15);
+      const int q = 4 * cur.ft + wn;
+      float h0[4], h1[4];
+      float am = 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float h0 = silu_mul(acc[i][0][v], acc[i][2][v]);
-        const float h1 = silu_mul(acc[i][1][v], acc[i][3][v]);
-        const float am = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
-        float mul;
-        const uint32_t sc = mx_scale_from_amax(am, &mul);
-        const int r = rbase + v;
-        if (r < cur.rows) {
-          auto* hrow = hq + (size_t)(cur.m0 + r) * I + q * 32 + (lane & 15);
-          const uint32_t c2 = f32x2_to_e4m3(h0 * mul, h1 * mul);
-          hrow[0] = (uint8_t)c2;
-          hrow[16] = (uint8_t)(c2 >> 8);
-          if ((lane & 15) == 0) hs[(size_t)(cur.m0 + r) * (I / 32) + q] = (uint8_t)sc;
-        }
+        h0[v] = silu_mul(acc[i][0][v], acc[i][2][v]);
+        h1[v] = silu_mul(acc[i][1][v], acc[i][3][v]);
+        am = fmaxf(am, fmaxf(fabsf(h0[v]), fabsf(h1[v])));
+      }
+      am = max_lanes_xor16_32(am);
+      float mul;
+      const uint32_t sc = mx_scale_from_amax(am, &mul);
+      if (r < cur.rows) {
+        auto* hrow = hq + (size_t)(cur.m0 + r) * I + q * 32 + 4 * g;
+        *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(hrow) =
+            f32x4_to_e4m3(h0[0] * mul, h0[1] * mul, h0[2] * mul, h0[3] * mul);
+        *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(hrow + 16) =
+            f32x4_to_e4m3(h1[0] * mul, h1[1] * mul, h1[2] * mul, h1[3] * mul);
+        if (g == 0) hs[(size_t)(cur.m0 + r) * (I / 32) + q] = (uint8_t)sc;
       }
     } else {
-      // The wave's 4 tiles are 64 consecutive columns (q2-groups g2, g2 + 1;
-      // H/32 is a multiple of 4, so both exist or neither does).  Each row's
-      // 128 bytes are written by 4 consecutive stores (t inner), which
-      // measured 4 % faster on the whole GEMM than finishing one tile's
-      // 4 rows at a time.
+      // lane holds token rows 16 (wm + 2i) + 4g + v, v < 4, column lane%16 of
+      // each tile.  The wave's 4 tiles are 64 consecutive columns (q2-groups
+      // g2, g2 + 1; H/32 is a multiple of 4, so both exist or neither does).
+      // Each row's 128 bytes are written by 4 consecutive stores (t inner),
+      // which measured 4 % faster on the whole GEMM than finishing one
+      // tile's 4 rows at a time.
+      const int rbase = 16 * (wm + 2 * i) + 4 * g;
       const int g2 = 8 * cur.ft + 2 * wn;
       if (g2 < QG2) {
 #pragma unroll
