@@ -143,9 +143,9 @@ def traffic_summary(fetch_dir: str, write_dir: str, kernel: str, workload: str, 
         "",
         "```",
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o f -- python3 bench.py "
-        f"--config {cfg} --steps {steps} --warmup 2 --cpu-budget 0 --copy-calibration",
+        f"--config {cfg} --decode-leg '' --steps {steps} --warmup 2 --cpu-budget 0 --copy-calibration",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o w -- python3 bench.py "
-        f"--config {cfg} --steps {steps} --warmup 2 --cpu-budget 0 --copy-calibration",
+        f"--config {cfg} --decode-leg '' --steps {steps} --warmup 2 --cpu-budget 0 --copy-calibration",
         f"python3 bench.py --traffic-summary {fetch_dir} {write_dir} --kernel '{kernel}' "
         f"--workload '{workload}' --config {cfg} --steps {steps}",
         "```",
@@ -198,7 +198,8 @@ def mfma_summary(pmc_dir: str, workload: str, cfg: str, steps: int) -> str:
         "",
         "```",
         f"rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES --output-format csv "
-        f"-d {pmc_dir} -o m -- python3 bench.py --config {cfg} --steps {steps} --warmup 2 --cpu-budget 0",
+        f"-d {pmc_dir} -o m -- python3 bench.py --config {cfg} --decode-leg '' --steps {steps} --warmup 2 "
+        f"--cpu-budget 0",
         f"python3 bench.py --mfma-summary {pmc_dir} --workload '{workload}' --config {cfg} --steps {steps}",
         "```",
         "",
