@@ -70,7 +70,7 @@ def rocprof_summary(paths) -> str:
             out.append("| kernel | calls | avg us | min us | max us | total ms | % |")
             out.append("|---|---|---|---|---|---|---|")
             for r in rows:
-                name = r["Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+                name = r["Name"].replace("moe::(anonymous namespace)::", "").replace("(anonymous namespace)::", "").split("(")[0]
                 out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                            f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                            f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
@@ -78,7 +78,7 @@ def rocprof_summary(paths) -> str:
         elif f.endswith("counter_collection.csv"):
             agg = {}
             for r in rows:
-                name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+                name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").replace("(anonymous namespace)::", "").split("(")[0]
                 key = (name, r["Counter_Name"])
                 agg.setdefault(key, []).append(float(r["Counter_Value"]))
             out.append(f"### counters per dispatch ({os.path.basename(f)})\n")
@@ -112,7 +112,7 @@ def _counter_means(path: str, counter: str):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != counter:
                 continue
-            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").replace("(anonymous namespace)::", "").split("(")[0]
             name = name.replace("void ", "")
             out.setdefault(name, []).append(float(r["Counter_Value"]))
     return out
@@ -186,7 +186,7 @@ def mfma_summary(pmc_dir: str, workload: str, cfg: str, steps: int) -> str:
     per = {}
     for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").split("(")[0]
+            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").replace("(anonymous namespace)::", "").split("(")[0]
             name = name.replace("void ", "")
             d = per.setdefault(name, {}).setdefault(r["Dispatch_Id"], {})
             d[r["Counter_Name"]] = float(r["Counter_Value"])

@@ -58,11 +58,12 @@ def build(verbose: bool = False) -> str:
     return SO
 
 
-# Stand-alone GPU check programs of the test suite (built here, on the CPU,
-# so that the GPU tests only run them).
+# Stand-alone GPU programs under tests/native, built here (on the CPU) so that
+# GPU runs only execute them: the conversion check of the test suite and the
+# two measurement probes whose rocprofv3 summaries are in profiles/.
 CHECKS = {
-    os.path.join(ROOT, "tests", "native", "cvt_equivalence.hip"):
-        os.path.join(ROOT, "tests", "native", "_build", "cvt_equivalence"),
+    os.path.join(ROOT, "tests", "native", name + ".hip"): os.path.join(ROOT, "tests", "native", "_build", name)
+    for name in ("cvt_equivalence", "hbm_stream", "mfma_rate")
 }
 
 
