@@ -583,15 +583,31 @@ __device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int b
 // (4 blocks of 32) of sorted row p, taken from row sorted_pair[p] / k of the
 // token-order scales (gate/up), or from row p (down, sorted_pair null).  A
 // tile's rows are consecutive sorted rows, so each K-step's scale loads then
-// read one contiguous run instead of one dword from each of 192 rows.
-__global__ __launch_bounds__(256) void scales_by_step_kernel(const uint32_t* __restrict__ src,
-                                                             int J, const int32_t* __restrict__ sorted_pair,
-                                                             int k, long P, uint32_t* __restrict__ sT) {
-  const long p = (long)blockIdx.x * 256 + threadIdx.x;
-  const int j = blockIdx.y;
+// read one contiguous run instead of one dword from each of 192 rows.  One
+// thread per sorted row reads the row's J dwords (16 bytes at a time when
+// vec: J a multiple of 4 and src 16-byte aligned, so every row is) and
+// writes K-step j's dword at sT[j][p], consecutive across the wave's lanes.
+__global__ __launch_bounds__(64) void scales_by_step_kernel(const uint32_t* __restrict__ src,
+                                                            int J, bool vec,
+                                                            const int32_t* __restrict__ sorted_pair,
+                                                            int k, long P, uint32_t* __restrict__ sT) {
+  const long p = (long)blockIdx.x * 64 + threadIdx.x;
   if (p >= P) return;
   const long row = sorted_pair ? (long)(sorted_pair[p] / k) : p;
-  sT[(size_t)j * P + p] = src[(size_t)row * J + j];
+  const uint32_t* s = src + (size_t)row * J;
+  uint32_t* d = sT + p;
+  if (vec) {
+#pragma unroll 4
+    for (int j = 0; j < J; j += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(s + j);
+      d[(size_t)j * P] = v.x;
+      d[(size_t)(j + 1) * P] = v.y;
+      d[(size_t)(j + 2) * P] = v.z;
+      d[(size_t)(j + 3) * P] = v.w;
+    }
+  } else {
+    for (int j = 0; j < J; ++j) d[(size_t)j * P] = s[j];
+  }
 }
 
 // kUp: gate/up GEMM (A = x rows gathered by token, K = H; B = W1/W3; epilogue
@@ -750,8 +766,9 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
   int* hdr = static_cast<int*>(tile_ws);
   uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, L.E, hdr);
-  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 255) / 256), (unsigned)L.J), dim3(256),
-                     0, s, reinterpret_cast<const uint32_t*>(xs), L.J, sorted_pair, k, P, sT);
+  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64)), dim3(64), 0, s,
+                     reinterpret_cast<const uint32_t*>(xs), L.J, L.J % 4 == 0 && (uintptr_t)xs % 16 == 0,
+                     sorted_pair, k, P, sT);
   const int NF = L.I / 128;
   KArgs a;
   a.wbase = packed + L.upw_off;
@@ -782,8 +799,9 @@ hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, con
   int* hdr = static_cast<int*>(tile_ws);
   uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, L.E, hdr);
-  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 255) / 256), (unsigned)L.J2), dim3(256),
-                     0, s, reinterpret_cast<const uint32_t*>(hs), L.J2, (const int32_t*)nullptr, k, P, sT);
+  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64)), dim3(64), 0, s,
+                     reinterpret_cast<const uint32_t*>(hs), L.J2, L.J2 % 4 == 0 && (uintptr_t)hs % 16 == 0,
+                     (const int32_t*)nullptr, k, P, sT);
   const int NF = (L.H + 255) / 256;
   KArgs a;
   a.wbase = packed + L.dnw_off;
