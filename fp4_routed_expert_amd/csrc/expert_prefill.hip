@@ -57,7 +57,7 @@
 // MFMA stream has no conditionals and only live accumulators are allocated.
 #include <atomic>
 
-#include "common.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
@@ -83,7 +83,6 @@ struct Stage {
 static_assert(sizeof(Stage) % 16 == 0, "stage alignment");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // An FP4 operand occupies the low 4 registers of the 8-register operand;
 // the upper half is left undefined so no registers are spent on it.
@@ -92,40 +91,6 @@ __device__ __forceinline__ v8i widen_fp4(uint4 b) {
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
-
-// Byte offset of 16-byte chunk c (0..7) of activation row r in a stage.
-__device__ __forceinline__ int a_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
-
-// LDS-DMA with a uniform 64-bit base in SGPRs and a per-lane 32-bit offset
-// (the saddr form): every lane loads 16 (or 4) bytes from base + its offset;
-// lane l's bytes land at LDS byte address m0 + 16 l (or 4 l).  The LDS
-// addresses are wave-uniform.  M0 is restored after; one wait state
-// separates each M0 write from the load that reads it.
-__device__ __forceinline__ void dma_x4(const uint8_t* base, uint32_t off, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds)
-      : "memory");
-}
-
-__device__ __forceinline__ void dma_x1(const uint8_t* base, uint32_t off, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds)
-      : "memory");
-}
 
 // The five 16-byte loads of a wave's stage (three activation row groups from
 // one base, two weight tiles from another) in one block, M0 saved once.
@@ -158,13 +123,6 @@ __device__ __forceinline__ void dma_stage5(const uint8_t* abase, uint32_t a0, ui
       : "memory");
 }
 
-// Wait until at most N of this wave's vector-memory loads are outstanding
-// (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                           int E, int* __restrict__ hdr) {
   __shared__ int cnt[1024];
@@ -192,15 +150,6 @@ struct Dma {
   uint32_t aoff[3];      // this lane's chunk of row groups w, w+8, w+16
   uint32_t soff;         // this lane's scale bytes
 };
-
-// Wave-uniform values for the scalar operands of the DMA instructions (no-ops
-// when the compiler already holds them in scalar registers).
-__device__ __forceinline__ uint32_t wave_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ const uint8_t* wave_ptr(const uint8_t* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint64_t lo = wave_u32((uint32_t)v), hi = wave_u32((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint8_t*>((uintptr_t)(lo | (hi << 32)));
-}
 
 // The per-wave constant part of the DMA: which scale load the wave issues
 // (0: none, 1: activation scale dwords, 2: weight scales as dwordx4), its

@@ -20,6 +20,7 @@
 // slice b % S and lands on XCD b % 8: with S a multiple of 4 each XCD reads
 // a fixed set of K columns of Wg into its L2 and reuses them for every token
 // tile, and the four waves of a workgroup share their x rows in L1.
+#include "lds_dma.h"
 #include "stages.h"
 
 namespace moe {
@@ -263,6 +264,152 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t* __res
     }
 }
 
+// ------------------------------------------------ LDS-DMA GEMM, large T, E >= 256
+// A workgroup (8 waves, 2 x 4) owns a 128-token x 256-expert tile and one K
+// slice.  Per stage of 64 K the tile's x rows (16 KB) and Wg rows (32 KB)
+// travel from global memory straight into LDS with LDS-DMA loads (every
+// lane writes 16 bytes; no register holds staged data), into a ring of three
+// stages.  A row's 128 bytes of a stage sit as eight 16-byte chunks, chunk c
+// at position c ^ (row & 7), so that the fragment reads of 16 consecutive
+// rows spread over the banks.  Each wave issues the same six loads per stage
+// (two x row groups, four Wg row groups of 8 rows; past the slice, its last
+// stage again, never read), so a stage is complete once at most six of the
+// wave's loads issued after it are outstanding.  Wave (wm, wn) multiplies
+// token rows 64 wm .. + 63 by expert rows 64 wn .. + 63: 4 x 4 blocks, two
+// MFMAs of 32 K (the stage's halves) each.  The K loop is software-pipelined
+// across the ring as in the FP4 expert GEMMs: a stage's first-half fragments
+// (the head) are read during the previous step, its second half (the tail)
+// at the start of its own step, behind the head's MFMAs; midway one barrier
+// publishes the next stage and frees the current slot, which takes the stage
+// three ahead, and the next head is read behind the tail's MFMAs.  Rows past
+// T or E are clamped to the last valid row and never stored.
+constexpr int kDM = 128;                       // tile rows (tokens)
+constexpr int kDN = 256;                       // tile columns (experts)
+constexpr int kDKB = 128;                      // bytes of a row per stage (64 bf16)
+constexpr int kDStage = (kDM + kDN) * kDKB;    // 48 KB
+constexpr int kDRing = 3;
+constexpr int kDOps = 6;                       // DMA loads per wave per stage
+
+struct RFrag {
+  v8bf a[4], b[4];
+};
+
+__global__ __launch_bounds__(512) void router_dma_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ wg, int T,
+                                                         int H, int E, int S,
+                                                         float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDRing * kDStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int NTm = (T + kDM - 1) / kDM, NTn = (E + kDN - 1) / kDN;
+  // block -> (slice, token tile, expert tile), slice-minor as in the tiled kernel
+  const int s = (int)(blockIdx.x % (unsigned)S);
+  const int tile = (int)(blockIdx.x / (unsigned)S);
+  const int tm = tile / NTn, tn = tile % NTn;
+  if (tm >= NTm) return;  // uniform per block: before any barrier
+  const int m0 = tm * kDM, n0 = tn * kDN;
+  const int nst = H / 64;
+  const int st0 = (int)(((long)s * nst) / S), n = (int)(((long)(s + 1) * nst) / S) - st0;
+
+  // DMA sources: lane l of row group rg loads row 8 rg + l / 8, logical chunk
+  // (l % 8) ^ (l / 8) (the row's low 3 bits are l / 8), which lands at
+  // physical chunk l % 8.  Offsets are from the slice's first K byte.
+  const uint32_t ch = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+  const uint32_t rowb = (uint32_t)H * 2u;
+  uint32_t xo[2], wo[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    xo[u] = (uint32_t)min(m0 + 8 * (wave + 8 * u) + (lane >> 3), T - 1) * rowb + ch;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    wo[u] = (uint32_t)min(n0 + 8 * (wave + 8 * u) + (lane >> 3), E - 1) * rowb + ch;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x) + (size_t)st0 * kDKB;
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(wg) + (size_t)st0 * kDKB;
+  const uint32_t ring = (uint32_t)(uintptr_t)(lds_u8*)lds;
+  auto issue = [&](int j) {
+    const int jj = min(j, n - 1);
+    const uint32_t st = wave_u32(ring + (uint32_t)(j % kDRing) * (uint32_t)kDStage);
+    const uint8_t* xs = wave_ptr(xb + (size_t)jj * kDKB);
+    const uint8_t* ws = wave_ptr(wb + (size_t)jj * kDKB);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma_x4(xs, xo[u], st + 1024u * (uint32_t)(wave + 8 * u));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dma_x4(ws, wo[u], st + (uint32_t)(kDM * kDKB) + 1024u * (uint32_t)(wave + 8 * u));
+  };
+
+  // fragment offsets: row 16-row block base + lane & 15, chunk g (first half
+  // of the stage) or g + 4 (second half)
+  const int fr = lane & 15, fg = lane >> 4;
+  const int fo0 = (fr * 128) + ((fg ^ (fr & 7)) << 4);
+  const int fo1 = (fr * 128) + (((fg + 4) ^ (fr & 7)) << 4);
+  const int abase = (64 * wm) * kDKB, bbase = kDM * kDKB + (64 * wn) * kDKB;
+  auto read = [&](RFrag& f, const uint8_t* S0, int fo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const v8bf*>(S0 + abase + 16 * kDKB * i + fo);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.b[i] = *reinterpret_cast<const v8bf*>(S0 + bbase + 16 * kDKB * i + fo);
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const RFrag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[q], acc[i][q], 0, 0, 0);
+  };
+
+  // Step j: stages up to j + 2 were issued before its barrier, so stage j + 1
+  // is complete once at most one stage of the wave's loads is outstanding.
+  auto step = [&](int j, const RFrag& hc, RFrag& hn) {
+    RFrag tl;
+    read(tl, lds + (j % kDRing) * kDStage, fo1);
+    mma(hc);
+    wait_vmcnt<kDOps>();
+    __syncthreads();  // stage j + 1 visible to all; every wave done with slot j
+    read(hn, lds + ((j + 1) % kDRing) * kDStage, fo0);
+    issue(j + kDRing);
+    mma(tl);
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  wait_vmcnt<2 * kDOps>();
+  __syncthreads();
+  RFrag h0, h1;
+  read(h0, lds, fo0);
+  int j = 0;
+  if (n & 1) {  // odd count: one step first, so the loop below takes steps in pairs
+    step(0, h0, h1);
+    h0 = h1;
+    j = 1;
+  }
+  for (; j < n; j += 2) {
+    step(j, h0, h1);
+    step(j + 1, h1, h0);
+  }
+  wait_vmcnt<0>();  // no LDS-DMA may still be writing when the workgroup's LDS is released
+
+  float* o = out + (S > 1 ? (size_t)s * T * E : 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = n0 + 64 * wn + 16 * q + fr;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = m0 + 64 * wm + 16 * i + 4 * fg + v;
+        if (t < T && e < E) o[(size_t)t * E + e] = acc[i][q][v];
+      }
+    }
+}
+
 // logits[i] = ((partial[0][i] + partial[1][i]) + ...) + partial[S-1][i], the
 // same order in which the routing kernels sum the partials they read directly
 __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, long n,
@@ -286,8 +433,13 @@ __global__ __launch_bounds__(256) void identity_route_kernel(int T, int32_t* __r
 
 int router_tm(int T) { return T <= 16 ? 1 : 4; }
 
-// Token counts from which the LDS-tiled kernel runs the GEMM.
+// Token counts from which the LDS-tiled kernels run the GEMM; the LDS-DMA
+// kernel takes over from 256 experts (its tile is 256 experts wide) while
+// the per-lane byte offsets of x fit 32 bits.
 constexpr int kTiledMinT = 128;
+bool router_dma(int T, int H, int E) {
+  return T >= kTiledMinT && E >= kDN && (long)T * H * 2 < (1L << 32) && (long)E * H * 2 < (1L << 32);
+}
 
 }  // namespace
 
@@ -300,6 +452,12 @@ constexpr int kTiledMinT = 128;
 // for that (multiple of 4).  Tiled (large T): as many slices as keep the
 // workgroups within one per compute unit (256).
 int router_slices(int T, int H, int E) {
+  if (router_dma(T, H, E)) {
+    const long tiles = (long)((T + kDM - 1) / kDM) * ((E + kDN - 1) / kDN);
+    const long want = 256 / tiles > 1 ? 256 / tiles : 1;
+    const int smax = H / 64 / 4 > 1 ? H / 64 / 4 : 1;
+    return (int)(want < smax ? want : smax);
+  }
   if (T >= kTiledMinT) {
     const long tiles = (long)((T + kTB - 1) / kTB) * ((E + kTB - 1) / kTB);
     const long want = 256 / tiles > 1 ? 256 / tiles : 1;
@@ -335,6 +493,12 @@ hipError_t launch_identity_route(int T, int32_t* sorted_pair, int32_t* offsets, 
 hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
                                   float* logits, float* partial, hipStream_t s) {
   const int S = router_slices(T, H, E);
+  if (router_dma(T, H, E)) {
+    const long tiles = (long)((T + kDM - 1) / kDM) * ((E + kDN - 1) / kDN);
+    hipLaunchKernelGGL(router_dma_kernel, dim3((unsigned)(tiles * S)), dim3(512), 0, s, x, wg, T,
+                       H, E, S, S > 1 ? partial : logits);
+    return hipGetLastError();
+  }
   if (T >= kTiledMinT) {
     const long tiles = (long)((T + kTB - 1) / kTB) * ((E + kTB - 1) / kTB);
     hipLaunchKernelGGL(router_tiled_kernel, dim3((unsigned)(tiles * S)), dim3(256), 2 * kTStage, s,

@@ -147,7 +147,9 @@ def test_router_and_shared_argument_errors():
     rws = L.moe_router_workspace_size(8, 4096, 64)
     # decode: the K range is split into slices whose fp32 partial sums live in the workspace
     assert rws >= 2 * 8 * 64 * 4 and rws % (8 * 64 * 4) == 0
-    assert L.moe_router_workspace_size(16384, 7168, 256) == 0   # enough output tiles: no split
+    # 128 output tiles of 128 x 256 fill half the chip: two K slices
+    assert L.moe_router_workspace_size(16384, 7168, 256) == 2 * 16384 * 256 * 4
+    assert L.moe_router_workspace_size(4096, 256, 1024) == 0     # K too short to split
     assert L.moe_router_workspace_size(8, 200, 64) == 0         # unsupported H
     assert rl(A, A, 4, 200, 8, A, A, 1 << 20, NUL) == UNS          # H % 128
     assert rl(A, A, 4, 256, 1025, A, A, 1 << 20, NUL) == UNS       # E > 1024

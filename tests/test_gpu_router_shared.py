@@ -65,9 +65,12 @@ ROUTER_SHAPES = [
     (64, 7168, 256),     # decode batch [56]
     (16, 7168, 256),     # decode, wide [16]
     (1000, 1024, 96),    # [4]
-    (4096, 256, 1024),   # enough output tiles: no K split [1]
+    (4096, 256, 1024),   # LDS-DMA GEMM (E >= 256), four expert tiles, no K split [1]
     (20, 256, 1024),     # the largest expert count, medium T [2]
-    (300, 128, 1000),    # tiled, ragged experts, two 64-K stages, no split [1]
+    (300, 128, 1000),    # LDS-DMA, ragged experts, two 64-K stages, no split [1]
+    (300, 512, 256),     # LDS-DMA, ragged tokens [2]
+    (777, 1536, 300),    # LDS-DMA, ragged tokens and experts, two expert tiles [6]
+    (129, 128, 256),     # LDS-DMA, one valid row in the second token tile [1]
 ]
 
 
@@ -98,9 +101,10 @@ def test_router_logits_full_prefill_size_sampled(dev):
     assert torch.equal(lg.cpu(), lg2.cpu())
 
 
-def test_router_one_hot_weights_return_the_activations(dev):
-    """Wg rows with a single +1: each logit is one activation, exactly."""
-    T, H, E = 40, 256, 24
+@pytest.mark.parametrize("T,H,E", [(40, 256, 24), (200, 512, 256)], ids=lambda v: str(v))
+def test_router_one_hot_weights_return_the_activations(T, H, E, dev):
+    """Wg rows with a single +1: each logit is one activation, exactly (the
+    register-staged and the LDS-DMA kernels)."""
     sh = synth.Shape(T=T, H=H, I=128, E=E, k=1, seed=77)
     x_bits, _ = synth.make_activations(sh)
     wg = np.zeros((E, H), dtype=np.uint16)
