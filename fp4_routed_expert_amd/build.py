@@ -63,7 +63,7 @@ def build(verbose: bool = False) -> str:
 # two measurement probes whose rocprofv3 summaries are in profiles/.
 CHECKS = {
     os.path.join(ROOT, "tests", "native", name + ".hip"): os.path.join(ROOT, "tests", "native", "_build", name)
-    for name in ("cvt_equivalence", "hbm_stream", "mfma_rate")
+    for name in ("cvt_equivalence", "hbm_stream", "mfma_rate", "lds_port")
 }
 
 
