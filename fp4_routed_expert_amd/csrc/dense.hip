@@ -292,6 +292,28 @@ __device__ __forceinline__ void dense_compute(v4f (&acc)[kSM][4], const uint8_t*
 // runs the whole pipeline below on its own share with its own two LDS
 // stages, and the groups' partial sums are added in group order at the end
 // (for tiles too few to give every CU one).
+// XCD-aware tile walk.  Workgroup b is dispatched to XCD b % 8; XCD x owns
+// the contiguous run [x per, (x + 1) per) (per = ceil(tiles / 8)) of the
+// tiles in panel order: column panels of SN = ceil(NTn / 4) weight-row tiles,
+// row-major inside a panel.  So the tiles an XCD runs at once form a compact
+// block (at 24 x 28 tiles: 12 token tiles x 7 row tiles per XCD) whose x rows
+// and weight rows its L2 shares, instead of every XCD reading every token
+// tile.  The grid is 8 per; a workgroup whose position is past the tiles
+// returns at once (false).
+__device__ __forceinline__ bool dense_tile_of(int NTm, int NTn, int b, int& bm, int& bn) {
+  const int tiles = NTm * NTn, per = (tiles + 7) / 8;
+  const int P = (b & 7) * per + (b >> 3);
+  if (P >= tiles) return false;
+  const int SN = (NTn + 3) / 4;
+  const int sc = P / (NTm * SN), q = P - sc * (NTm * SN);
+  const int w = min(SN, NTn - sc * SN);
+  bm = q / w;
+  bn = sc * SN + q % w;
+  return true;
+}
+
+long dense_grid(long tiles) { return 8 * ((tiles + 7) / 8); }
+
 template <int kWM, int kWN, int kSM, int kSets, int kSplit>
 __global__ __launch_bounds__(64 * kWM * kWN * kSplit) void dense_prefill_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ xq,
@@ -309,9 +331,9 @@ __global__ __launch_bounds__(64 * kWM * kWN * kSplit) void dense_prefill_kernel(
   const int lane = tid & 63, wave = tid >> 6;   // wave within the group
   const int wm = wave / kWN, wn = wave % kWN;
   const int NTn = (N + 16 * C::BT - 1) / (16 * C::BT);
-  // weight-row tiles vary fastest: the token tile's x rows stay in L2 while its
-  // row tiles go by, consecutive workgroups of an XCD (block % 8) share them
-  const int bn = (int)(blockIdx.x % (unsigned)NTn), bm = (int)(blockIdx.x / (unsigned)NTn);
+  const int NTm = (T + C::BM - 1) / C::BM;
+  int bm, bn;
+  if (!dense_tile_of(NTm, NTn, (int)blockIdx.x, bm, bn)) return;  // uniform: before any barrier
   const int m0 = bm * C::BM, nt0 = bn * C::BT;  // first token, first 16-row weight tile
   const int ntiles = N / 16;
   // this group's K-steps [j0, J) (J re-based as its end); steps past it load
@@ -516,15 +538,15 @@ hipError_t launch_dense_prefill(const uint8_t* packed, const uint8_t* xq, const 
   if (116 * rounds_large < 100 * rounds_small) {
     const long blocks = (long)((T + DLarge::BM - 1) / DLarge::BM) *
                         ((N + 16 * DLarge::BT - 1) / (16 * DLarge::BT));
-    hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets, 1>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets, 1>), dim3((unsigned)dense_grid(blocks)),
                        dim3(DLarge::NT), 0, s,
                        packed, xq, xs, T, N, K, y);
   } else if (wg_small <= occ.ncu) {
     // fewer small tiles than CUs: each tile's K-steps split over two wave groups
-    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2, 2>), dim3((unsigned)wg_small),
+    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2, 2>), dim3((unsigned)dense_grid(wg_small)),
                        dim3(2 * DSmall::NT), 0, s, packed, xq, xs, T, N, K, y);
   } else {
-    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2, 1>), dim3((unsigned)wg_small),
+    hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2, 1>), dim3((unsigned)dense_grid(wg_small)),
                        dim3(DSmall::NT), 0, s, packed, xq, xs, T, N, K, y);
   }
   return hipGetLastError();
