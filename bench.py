@@ -43,6 +43,7 @@ HBM_PEAK_GBS = 8000.0
 DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true, 1>"   # the instantiations the library launches
 DENSE_PREFILL_KERNEL = "dense_prefill_kernel<2, 4, 6, 2, 1>"  # (prefill: the 192 x 256 tile)
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 (and FP8 x FP4 scaled MFMA at the FP8 issue rate)
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense FP4 x FP4 (reported beside: the mixed FP8 x FP4 MFMA issues at the FP8 rate)
 METRIC = "MoE-layer tokens/s + achieved HBM TB/s (decode) / MFMA util (prefill), 1 GPU"
 
@@ -724,10 +725,14 @@ def measure_layer(args, cfg: str, steps: int, warmup: int) -> dict:
         r_gbs = r_bytes / (r_ms * 1e-3) / 1e9
         line["config"]["workload"] += f" + router GEMM + {ns} shared expert(s)"
         line["config"]["n_shared"] = ns
-        line["router"] = {"bound": "hbm", "kernel": "router_partial_kernel + router_reduce_kernel (bf16 x . Wg, fp32 logits)",
+        r_kernel = ("router_dma_kernel" if T >= 128 and E >= 256 else
+                    "router_tiled_kernel" if T >= 128 else "router_partial_kernel")
+        r_tflops = 2.0 * T * H * E / (r_ms * 1e-3) / 1e12
+        line["router"] = {"bound": "hbm", "kernel": f"{r_kernel} + slice sum (bf16 x . Wg, fp32 logits)",
                           "achieved": r_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": r_gbs / HBM_PEAK_GBS, "alg_bytes_per_launch": r_bytes,
-                          "alg_flops_per_launch": 2.0 * T * H * E, "avg_launch_us": r_ms * 1e3}
+                          "alg_flops_per_launch": 2.0 * T * H * E, "avg_launch_us": r_ms * 1e3,
+                          "tflops": r_tflops, "frac_of_bf16_peak": r_tflops / MFMA_BF16_PEAK_TFLOPS}
         line["layer_hbm_tbps"] = (b_layer + E * H * 2) / (ms_per_step * 1e-3) / 1e12
         line["layer_hbm_frac"] = line["layer_hbm_tbps"] * 1e3 / HBM_PEAK_GBS
     return line

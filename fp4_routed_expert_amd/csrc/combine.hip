@@ -3,9 +3,8 @@
 // j = 0..k-1 (then the shared row) in fp32 with no atomics (a fixed
 // reduction order, pwwt.cn review section 4.2).  O holds the expert outputs
 // as bf16 (a matrix-multiply output kept at low precision, its sum in fp32:
-// the same review, section 4.1).  Each thread produces eight consecutive
-// outputs from 128-bit loads of O and two 128-bit stores (four from 64-bit
-// loads when H or the alignment does not allow it); bandwidth bound at
+// the same review, section 4.1).  Each thread produces four consecutive
+// outputs from 64-bit loads of O and one 128-bit store; bandwidth bound at
 // prefill sizes, latency bound at decode sizes (hence the batched loads).
 #include "common.h"
 
@@ -63,72 +62,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint2* __restrict__ 
   __builtin_nontemporal_store(v4f{acc.x, acc.y, acc.z, acc.w}, reinterpret_cast<v4f*>(y + (size_t)t * H4 + c));
 }
 
-// The same sum with eight consecutive outputs per thread: one 16-byte load
-// of O per slot (twice the bytes in flight per load) and two 16-byte stores
-// of y.  Taken when H % 8 == 0 and O (and the shared rows) are 16-byte
-// aligned; the order of the sums is the same, so the result is bitwise equal.
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-__global__ __launch_bounds__(128) void combine8_kernel(const uint4* __restrict__ O,
-                                                       const float* __restrict__ gates,
-                                                       const int32_t* __restrict__ pair_pos,
-                                                       const uint4* __restrict__ Os, int k, int H8,
-                                                       float4* __restrict__ y) {
-  const int t = blockIdx.x;
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
-  if (c >= H8) return;
-  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    const int n = min(8, k - j0);
-    int row[8];
-    float g[8];
-    v4u o[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const size_t idx = (size_t)t * k + j0 + min(u, n - 1);
-      row[u] = pair_pos[idx];
-      g[u] = gates[idx];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      o[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(O + (size_t)row[u] * H8 + c));
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < n) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          a[2 * w] = fmaf(g[u], bf16_lo(o[u][w]), a[2 * w]);
-          a[2 * w + 1] = fmaf(g[u], bf16_hi(o[u][w]), a[2 * w + 1]);
-        }
-      }
-    }
-  }
-  if (Os) {  // the shared expert, weight 1, after the routed slots
-    const uint4 o = Os[(size_t)t * H8 + c];
-    const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      a[2 * w] += bf16_lo(ow[w]);
-      a[2 * w + 1] += bf16_hi(ow[w]);
-    }
-  }
-  v4f* yr = reinterpret_cast<v4f*>(y + (size_t)t * 2 * H8 + 2 * c);
-  __builtin_nontemporal_store(v4f{a[0], a[1], a[2], a[3]}, yr);
-  __builtin_nontemporal_store(v4f{a[4], a[5], a[6], a[7]}, yr + 1);
-}
-
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos,
                           const uint16_t* O_shared, int T, int k, int H, float* y, hipStream_t s) {
-  if (H % 8 == 0 && (uintptr_t)O % 16 == 0 && (uintptr_t)O_shared % 16 == 0) {
-    const int H8 = H / 8;
-    dim3 grid((unsigned)T, (unsigned)((H8 + 127) / 128));
-    hipLaunchKernelGGL(combine8_kernel, grid, dim3(128), 0, s, reinterpret_cast<const uint4*>(O),
-                       gates, pair_pos, reinterpret_cast<const uint4*>(O_shared), k, H8,
-                       reinterpret_cast<float4*>(y));
-    return hipGetLastError();
-  }
   const int H4 = H / 4;
   dim3 grid((unsigned)T, (unsigned)((H4 + 255) / 256));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, reinterpret_cast<const uint2*>(O),
