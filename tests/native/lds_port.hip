@@ -6,11 +6,13 @@
 // DMAs one 48 KiB stage (six 1 KiB loads per wave, two stages in flight)
 // from an L2-resident 2 MiB window and/or reads 128 KiB (sixteen 1 KiB reads
 // per wave) from the stage written two iterations earlier; one barrier per
-// iteration.  Also: the same DMA from a 1.4 GiB buffer read as rows 14 KiB
-// apart (an HBM stream, 8 rows of 128 bytes per load, like the x rows of a
-// K-step), and the time an LDS read issued right after the same wave's
-// LDS-DMA load takes to return.  Prints one line per case; the best of five
-// launches.  Measurement only: checks nothing.
+// iteration.  Also: the raw read rate (batches of sixteen 128-bit reads per
+// wave with no barrier, alone and beside 8 or 16 KiB of DMA per batch), the
+// same DMA from a 1.4 GiB buffer read as rows 14 KiB apart (an HBM stream, 8
+// rows of 128 bytes per load, like the x rows of a K-step), and the time an
+// LDS read issued right after the same wave's LDS-DMA load takes to return.
+// Prints one line per case; the best of five launches.  Measurement only:
+// checks nothing.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -68,6 +70,44 @@ __global__ __launch_bounds__(512) void lds_traffic(const uint8_t* __restrict__ s
   }
   wait_vmcnt<0>();
   if (acc == 0x9E3779B9u) sink[tid] = acc;  // keeps the reads
+}
+
+// Raw read rate: per batch each wave issues 16 reads of 1 KiB with no
+// barrier; NDMA (0, 1, 2) 1 KiB DMA loads per wave per batch go to a third
+// slot that is never read, at most 8 in flight.
+template <int NDMA>
+__global__ __launch_bounds__(512) void lds_raw(const uint8_t* __restrict__ src, int iters,
+                                               uint32_t* __restrict__ sink) {
+  __shared__ __align__(16) uint8_t lds[3 * kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < 3 * kStage / 16; i += 512) reinterpret_cast<uint4*>(lds)[i] = make_uint4(i, 1, 2, 3);
+  __syncthreads();
+  const uint32_t ring = (uint32_t)(uintptr_t)(lds_u8*)lds;
+  const uint8_t* win = src + (size_t)(blockIdx.x & 7) * (2u << 20);
+  uint4 a = make_uint4(0, 0, 0, 0);
+  for (int it = 0; it < iters; ++it) {
+    if (NDMA > 0) {
+      const uint8_t* tb = wave_ptr(win + (size_t)(((blockIdx.x >> 3) + it) % 1000) * 2048);
+      dma_x4(tb, (uint32_t)(lane * 16), wave_u32(ring + 2u * kStage + (uint32_t)((wave * 6 + (it % 6)) * 1024)));
+      if (NDMA > 1)
+        dma_x4(tb, (uint32_t)(1024 + lane * 16),
+               wave_u32(ring + 2u * kStage + (uint32_t)((wave * 6 + ((it + 3) % 6)) * 1024)));
+      wait_vmcnt<8>();
+    }
+    asm volatile("" ::: "memory");  // the reads are redone every batch
+    const uint8_t* rs = lds + (it & 1) * kStage;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint4 v = *reinterpret_cast<const uint4*>(rs + ((wave * 16 + u) * 1024 + lane * 16) % kStage);
+      a.x ^= v.x;
+      a.y ^= v.y;
+      a.z ^= v.z;
+      a.w ^= v.w;
+    }
+  }
+  wait_vmcnt<0>();
+  if ((a.x ^ a.y ^ a.z ^ a.w) == 0x9E3779B9u) sink[tid] = a.x;
 }
 
 // One wave per workgroup: an LDS-DMA load of a cold 4 KiB slice, then a
@@ -167,6 +207,31 @@ bool traffic(const char* name, const uint8_t* src, uint32_t* sink, int ncu, doub
   return true;
 }
 
+template <int NDMA>
+bool raw(const char* name, const uint8_t* src, uint32_t* sink, int ncu) {
+  const int iters = 4000;
+  hipEvent_t a, b;
+  if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return false;
+  hipLaunchKernelGGL(lds_raw<NDMA>, dim3(ncu), dim3(512), 0, 0, src, 100, sink);
+  if (!ok(hipDeviceSynchronize(), "warm-up")) return false;
+  float best = 1e30f;
+  for (int rep = 0; rep < 5; ++rep) {
+    hipEventRecord(a);
+    hipLaunchKernelGGL(lds_raw<NDMA>, dim3(ncu), dim3(512), 0, 0, src, iters, sink);
+    hipEventRecord(b);
+    if (!ok(hipEventSynchronize(b), name)) return false;
+    float ms = 0;
+    hipEventElapsedTime(&ms, a, b);
+    best = std::min(best, ms);
+  }
+  const double us = best * 1e3 / iters;
+  std::printf("%-46s %8.4f us/batch  reads %6.1f GB/s per CU, DMA %5.1f GB/s per CU\n", name, us,
+              128.0 * 1024 / us / 1e3, 8.0 * NDMA * 1024 / us / 1e3);
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  return true;
+}
+
 template <bool kDma>
 bool order(const char* name, const uint8_t* src, unsigned long long* d_out, unsigned long long* h) {
   const int nblk = 256, iters = 64;
@@ -203,6 +268,10 @@ int main() {
       !traffic<1>("ds_read_b128 128 KiB/iteration", src, sink, ncu, 128) ||
       !traffic<2>("both: DMA 48 KiB + reads 128 KiB", src, sink, ncu, 176) ||
       !traffic<3>("DMA 48 KiB/iteration, row-strided HBM stream", src, sink, ncu, 48))
+    return 1;
+  if (!raw<0>("raw reads, 128 KiB per batch, no barrier", src, sink, ncu) ||
+      !raw<1>("raw reads + 8 KiB DMA per batch", src, sink, ncu) ||
+      !raw<2>("raw reads + 16 KiB DMA per batch", src, sink, ncu))
     return 1;
   if (!order<false>("LDS read alone", src, d_out, h) || !order<true>("LDS read right after an LDS-DMA load", src, d_out, h))
     return 1;
