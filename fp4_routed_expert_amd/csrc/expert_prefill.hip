@@ -43,10 +43,12 @@
 // A K-step is software-pipelined across the LDS ring: its weight fragments
 // and first half of activation fragments (the head) were read from LDS during
 // the previous step; the rest (the tail) are read at its start, behind the
-// head's MFMAs; midway, one barrier publishes the next stage and retires the
-// current slot, which is refilled at once, and the next head is read behind
-// the tail's MFMAs.  So LDS reads, DMA issue and the barrier all overlap
-// MFMA work, and the loop body has no branches.
+// head's MFMAs; midway, one barrier publishes the next stage and frees the
+// current slot, which is refilled, and the next head is read -- before the
+// tail's MFMAs by one wave of each SIMD, after them by the other, so that
+// the two waves' LDS reads and DMA issue do not coincide and one of them
+// keeps the matrix pipe busy.  So LDS reads, DMA issue and the barrier all
+// overlap MFMA work; the loop's only branches are on the wave's token half.
 //
 // Waves form a 2 (tokens) x 4 (features) grid, wm = wave / 4 so that each
 // SIMD holds one wave of each token half: a wave owns the 16-row sub-tiles
@@ -345,7 +347,12 @@ __device__ __forceinline__ __attribute__((address_space(1))) T* as_global(T* p) 
 // sorted order, rows past the tile repeating the last.
 template <bool kUp>
 __device__ __forceinline__ void make_dma(Item& it, const int* rsrc, const KArgs& a, int wave,
-                                         int lane) {
+                                         int lane_) {
+  // Down GEMM: the lane index recomputed here from the exec mask (all lanes
+  // are active; the asm is not hoisted), so that no register carries it
+  // across the K loop -- the down kernel's register budget is full.
+  int lane = lane_;
+  if (!kUp) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   Dma& d = it.d;
   const int K = kUp ? a.H : a.I;
   const int e = it.e, m0 = it.m0, rows = it.rows, ft = it.ft;
@@ -445,9 +452,21 @@ __device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int b
     if constexpr (N > 0) mfma_head<kUp, N>(hc, acc);
     wait_vmcnt<kOps>();
     __syncthreads();
-    if constexpr (N > 0) read_head<kUp, N>(hn, Sn, o);
-    issue(j + kRing);
+    // The two waves of a SIMD (token halves wm 0 and 1) take the memory work
+    // of the step at different points: wm 0 reads the next head and issues
+    // its DMA right after the barrier, then runs the tail MFMAs; wm 1 runs
+    // its tail MFMAs first.  So while one wave of a SIMD waits on LDS reads
+    // and DMA issue the other keeps the matrix pipe busy, instead of all 8
+    // waves doing both at the same moment after the barrier.
+    if (wm == 0) {
+      if constexpr (N > 0) read_head<kUp, N>(hn, Sn, o);
+      issue(j + kRing);
+    }
     if constexpr (N > 0) mfma_tail<kUp, N>(hc, tl, acc);
+    if (wm != 0) {
+      if constexpr (N > 0) read_head<kUp, N>(hn, Sn, o);
+      issue(j + kRing);
+    }
   };
   if (!primed) {  // cold start: fill the ring and wait for stage 0
     issue(0);
