@@ -85,16 +85,18 @@ def test_router_logits_within_fp32_bound(T, H, E, dev):
     _check_logits(lg.cpu().numpy(), x_bits, wg_bits, f"router T{T} H{H} E{E}")
 
 
-def test_router_logits_full_prefill_size_sampled(dev):
-    """T 4604, H 7168, E 256 (the large prefill workload's router) on sampled tokens."""
-    sh = synth.CONFIGS["c3"]
-    log("[router] c3 sampled")
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_router_logits_full_prefill_size_sampled(name, dev):
+    """The prefill workloads' routers on sampled tokens: T 4604 (7 K slices)
+    and T 16384 (2 K slices), H 7168, E 256."""
+    sh = synth.CONFIGS[name]
+    log(f"[router] {name} sampled")
     x_bits, _ = synth.make_activations(sh)
     wg_bits = synth.make_router_weights(sh)
     lg = moe.router_logits(_bf16_dev(x_bits, dev), _bf16_dev(wg_bits, dev))
     torch.cuda.synchronize()
     toks = sample_tokens(sh.T, 48, seed=9)
-    _check_logits(lg.cpu().numpy()[toks], x_bits[toks], wg_bits, "router c3")
+    _check_logits(lg.cpu().numpy()[toks], x_bits[toks], wg_bits, f"router {name}")
     # repeatable: the same call gives the same bits
     lg2 = moe.router_logits(_bf16_dev(x_bits, dev), _bf16_dev(wg_bits, dev))
     torch.cuda.synchronize()
