@@ -60,9 +60,9 @@ def test_route_argument_errors():
 
 
 def test_sort_argument_errors():
-    assert L.moe_sort_permute_workspace_size(16, 8, 2) == 0       # one chunk: no workspace
+    assert L.moe_sort_permute_workspace_size(16, 8, 2) == 0       # one workgroup: no workspace
     need = L.moe_sort_permute_workspace_size(16384, 256, 8)
-    assert need == 32 * 256 * 4
+    assert need == 64 * 256 * 4                                  # 64 chunks of 2048 pairs
     assert L.moe_sort_permute(A, 16384, 256, 8, A, A, A, A, A, need - 1, NUL) == WSE
     assert L.moe_sort_permute(A, 16384, 256, 8, A, A, A, A, NUL, need, NUL) == WSE
     assert L.moe_sort_permute(A, 16384, 256, 8, A, A, A, A, MIS, need, NUL) == INV
