@@ -247,6 +247,11 @@ hipError_t launch_front_small(const float* logits, int S, const uint16_t* x, int
                               uint8_t* xq, uint8_t* xs, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int S, int T, int E, int k, int ns,
                              int32_t* ids, float* gates, hipStream_t s);
+// Routing (as launch_route_topk) and MXFP8 quantisation of x [T, H] (as
+// launch_quant_mxfp8) in one launch, for batches above kFrontMaxT.
+hipError_t launch_front_route_quant(const float* logits, int S, const uint16_t* x, int T, int H,
+                                    int E, int k, int ns, int32_t* ids, float* gates, uint8_t* xq,
+                                    uint8_t* xs, hipStream_t s);
 size_t sort_workspace_bytes(int T, int E, int k);
 hipError_t launch_sort_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
                                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,

@@ -117,10 +117,11 @@ LayerCarve layer_carve(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
 }
 
 // Steps 1-3 of the layer into the carve's buffers: one fused launch for
-// T <= kFrontMaxT, else the stand-alone routing, sort and quantisation.  The
-// logits are S planes summed in order (S = 1: plain logits); routing is over
-// E experts, with ns shared experts (E .. E+ns-1, weight 1) appended as slots
-// k .. k+ns-1 of every token; c is the carve for k + ns slots and E + ns experts.
+// T <= kFrontMaxT, else routing and quantisation in one launch, then the
+// sort.  The logits are S planes summed in order (S = 1: plain logits);
+// routing is over E experts, with ns shared experts (E .. E+ns-1, weight 1)
+// appended as slots k .. k+ns-1 of every token; c is the carve for k + ns
+// slots and E + ns experts.
 moe_status_t run_front(const float* logits, int S, const uint16_t* x_bf16, int32_t T, int32_t H,
                        int32_t E, int32_t k, int32_t ns, uint8_t* ws, const LayerCarve& c,
                        hipStream_t stream) {
@@ -135,11 +136,11 @@ moe_status_t run_front(const float* logits, int S, const uint16_t* x_bf16, int32
   if (T <= kFrontMaxT)
     return hip_status(launch_front_small(logits, S, x_bf16, T, H, E, k, ns, ids, gates, counts,
                                          offsets, sorted, pos, xq, xs, stream));
-  moe_status_t st = hip_status(launch_route_topk(logits, S, T, E, k, ns, ids, gates, stream));
+  moe_status_t st = hip_status(
+      launch_front_route_quant(logits, S, x_bf16, T, H, E, k, ns, ids, gates, xq, xs, stream));
   if (st == MOE_OK)
     st = hip_status(launch_sort_permute(ids, T, E + ns, k + ns, counts, offsets, sorted, pos,
                                         ws + c.sort_ws, stream));
-  if (st == MOE_OK) st = hip_status(launch_quant_mxfp8(x_bf16, T, H, xq, xs, stream));
   return st;
 }
 
