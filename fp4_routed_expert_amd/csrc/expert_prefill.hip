@@ -125,20 +125,51 @@ __device__ __forceinline__ void dma_stage5(const uint8_t* abase, uint32_t a0, ui
       : "memory");
 }
 
-__global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                          int E, int* __restrict__ hdr) {
-  __shared__ int cnt[1024];
-  __shared__ int wave_tot[4];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) cnt[e] = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
-  __syncthreads();
-  const int total = block_exclusive_scan256(cnt, E, wave_tot);
+// The token-tile list, built by one wave: tiles of kBM sorted rows, expert by
+// expert in order (tile (e, o0 + i kBM) for i < ceil(rows_e / kBM)); the
+// count at hdr[0], the (expert, first row) pairs from byte kTileHdr.  Round j
+// takes experts 64 j .. 64 j + 63, one per lane: a wave-wide inclusive scan of
+// their tile counts, on top of the rounds before, places each expert's tiles;
+// then the wave writes the round's tiles 64 at a time, each lane finding the
+// expert of its tile by binary search over the scan (an expert with many
+// tiles is not left to one lane).
+__device__ void build_tiles_wave(const int32_t* __restrict__ offsets, int E, int* __restrict__ hdr) {
+  const int lane = threadIdx.x & 63;
   int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<uint8_t*>(hdr) + kTileHdr);
-  for (int e = tid; e < E; e += 256) {
-    const int o0 = offsets[e], n = (offsets[e + 1] - o0 + kBM - 1) / kBM;
-    for (int i = 0; i < n; ++i) tiles[cnt[e] + i] = make_int2(e, o0 + i * kBM);
+  // every round's offsets in one batch of loads (E <= 1024: at most 16 rounds)
+  constexpr int kRounds = 16;
+  int lo_off[kRounds], hi_off[kRounds];
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    lo_off[j] = offsets[min(64 * j + lane, E)];
+    hi_off[j] = offsets[min(64 * j + lane + 1, E)];
   }
-  if (tid == 0) hdr[0] = total;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int e0 = 64 * j;
+    if (e0 >= E) break;
+    const int o0 = lo_off[j];
+    const int m = (hi_off[j] - o0 + kBM - 1) / kBM;  // 0 past the last expert
+    int incl = m;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int n = __shfl(incl, 63);
+    for (int i0 = 0; i0 < n; i0 += 64) {  // uniform: every lane takes part in the shuffles
+      const int i = i0 + lane;
+      int lo = 0;  // first lane whose inclusive count exceeds i (63 when i >= n)
+#pragma unroll
+      for (int step = 32; step > 0; step >>= 1)
+        if (__shfl(incl, lo + step - 1) <= i) lo += step;
+      const int first = __shfl(incl - m, lo), row0 = __shfl(o0, lo);
+      if (i < n) tiles[base + i] = make_int2(e0 + lo, row0 + (i - first) * kBM);
+    }
+    base += n;
+  }
+  if (lane == 0) hdr[0] = base;
 }
 
 // One wave's share of the DMA loads of a stage, the part that changes from
@@ -555,11 +586,19 @@ __device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int b
 // thread per sorted row reads the row's J dwords (16 bytes at a time when
 // vec: J a multiple of 4 and src 16-byte aligned, so every row is) and
 // writes K-step j's dword at sT[j][p], consecutive across the wave's lanes.
+// With hdr set, the launch's first workgroup builds the token-tile list
+// instead (hdr null: the list is already built).
 __global__ __launch_bounds__(64) void scales_by_step_kernel(const uint32_t* __restrict__ src,
                                                             int J, bool vec,
                                                             const int32_t* __restrict__ sorted_pair,
-                                                            int k, long P, uint32_t* __restrict__ sT) {
-  const long p = (long)blockIdx.x * 64 + threadIdx.x;
+                                                            int k, long P, uint32_t* __restrict__ sT,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int E, int* __restrict__ hdr) {
+  if (hdr && blockIdx.x == 0) {
+    build_tiles_wave(offsets, E, hdr);
+    return;
+  }
+  const long p = (long)(blockIdx.x - (hdr ? 1 : 0)) * 64 + threadIdx.x;
   if (p >= P) return;
   const long row = sorted_pair ? (long)(sorted_pair[p] / k) : p;
   const uint32_t* s = src + (size_t)row * J;
@@ -733,10 +772,9 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
   const long P = (long)T * k;
   int* hdr = static_cast<int*>(tile_ws);
   uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, L.E, hdr);
-  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64)), dim3(64), 0, s,
+  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64 + 1)), dim3(64), 0, s,
                      reinterpret_cast<const uint32_t*>(xs), L.J, L.J % 4 == 0 && (uintptr_t)xs % 16 == 0,
-                     sorted_pair, k, P, sT);
+                     sorted_pair, k, P, sT, offsets, L.E, hdr);
   const int NF = L.I / 128;
   KArgs a;
   a.wbase = packed + L.upw_off;
@@ -762,14 +800,14 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
 
 hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
                                const uint8_t* hs, const int32_t* offsets, int T, int k, uint16_t* O,
-                               void* tile_ws, hipStream_t s) {
+                               void* tile_ws, bool tiles_ready, hipStream_t s) {
   const long P = (long)T * k;
   int* hdr = static_cast<int*>(tile_ws);
   uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, L.E, hdr);
-  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64)), dim3(64), 0, s,
-                     reinterpret_cast<const uint32_t*>(hs), L.J2, L.J2 % 4 == 0 && (uintptr_t)hs % 16 == 0,
-                     (const int32_t*)nullptr, k, P, sT);
+  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64 + (tiles_ready ? 0 : 1))),
+                     dim3(64), 0, s, reinterpret_cast<const uint32_t*>(hs), L.J2,
+                     L.J2 % 4 == 0 && (uintptr_t)hs % 16 == 0, (const int32_t*)nullptr, k, P, sT,
+                     offsets, L.E, tiles_ready ? nullptr : hdr);
   const int NF = (L.H + 255) / 256;
   KArgs a;
   a.wbase = packed + L.dnw_off;

@@ -301,10 +301,14 @@ moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, co
                                      decode_row_groups((int64_t)T * k, w->E), stream));
 }
 
-moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, const uint8_t* hs,
-                                 const int32_t* expert_offsets, int32_t T, int32_t k, uint16_t* O,
-                                 void* workspace, size_t workspace_bytes, uint32_t flags,
-                                 hipStream_t stream) {
+}  // extern "C"
+
+// The down stage; tiles_ready: the gate/up stage of the same call just ran
+// with this workspace and these offsets, so its token-tile list is reused.
+static moe_status_t expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, const uint8_t* hs,
+                                const int32_t* expert_offsets, int32_t T, int32_t k, uint16_t* O,
+                                void* workspace, size_t workspace_bytes, uint32_t flags,
+                                bool tiles_ready, hipStream_t stream) {
   moe_status_t st = check_weights(w);
   if (st != MOE_OK) return st;
   st = check_tek(T, w->E, k);
@@ -319,9 +323,20 @@ moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, 
   const PackedLayout L(w->E, w->H, w->I);
   const uint8_t* pk = static_cast<const uint8_t*>(w->packed);
   if (path == 1)
-    return hip_status(launch_down_prefill(pk, L, hq, hs, expert_offsets, T, k, O, workspace, stream));
+    return hip_status(launch_down_prefill(pk, L, hq, hs, expert_offsets, T, k, O, workspace,
+                                          tiles_ready, stream));
   return hip_status(launch_down_decode(pk, L, hq, hs, expert_offsets, O,
                                        decode_row_groups((int64_t)T * k, w->E), stream));
+}
+
+extern "C" {
+
+moe_status_t moe_fp4_expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, const uint8_t* hs,
+                                 const int32_t* expert_offsets, int32_t T, int32_t k, uint16_t* O,
+                                 void* workspace, size_t workspace_bytes, uint32_t flags,
+                                 hipStream_t stream) {
+  return expert_down(w, hq, hs, expert_offsets, T, k, O, workspace, workspace_bytes, flags, false,
+                     stream);
 }
 
 moe_status_t moe_combine(const uint16_t* O, const float* topk_gates, const int32_t* pair_pos,
@@ -368,7 +383,7 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w, const uint8_t* 
   st = moe_fp4_expert_up(w, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs, stage,
                          stage_bytes, flags, stream);
   if (st != MOE_OK) return st;
-  st = moe_fp4_expert_down(w, hq, hs, expert_offsets, T, k, O, stage, stage_bytes, flags, stream);
+  st = expert_down(w, hq, hs, expert_offsets, T, k, O, stage, stage_bytes, flags, true, stream);
   if (st != MOE_OK) return st;
   return moe_combine(O, topk_gates, pair_pos, T, k, w->H, y, stream);
 }
@@ -532,8 +547,8 @@ moe_status_t moe_fp4_shared_expert(const moe_fp4_weights_t* w, const uint8_t* xq
   st = moe_fp4_expert_up(w, xq, xs, offsets, sorted, T, 1, ws + c.hq, ws + c.hs, ws + c.stage,
                          c.total - c.stage, flags, stream);
   if (st != MOE_OK) return st;
-  return moe_fp4_expert_down(w, ws + c.hq, ws + c.hs, offsets, T, 1, O_shared, ws + c.stage,
-                             c.total - c.stage, flags, stream);
+  return expert_down(w, ws + c.hq, ws + c.hs, offsets, T, 1, O_shared, ws + c.stage,
+                     c.total - c.stage, flags, true, stream);
 }
 
 moe_status_t moe_combine_shared(const uint16_t* O, const float* topk_gates, const int32_t* pair_pos,
