@@ -44,6 +44,30 @@ def test_route_sort_quant_bit_exact(name, dev):
     assert got == GOLDEN[name]
 
 
+# (T, k, E, heavy): pair counts on both sides of the one-workgroup limit (4096)
+# and of each chunk-size step (1024 / 2048 / 4096 pairs per chunk, about 64
+# chunks), a chunk count that leaves a short last batch of the scan, E not a
+# multiple of the 256 scan threads, and three quarters of the pairs on one expert.
+SORT_SIZES = [(512, 8, 256, False), (4097, 1, 256, False), (8192, 8, 256, False),
+              (65537, 1, 1000, False), (32769, 8, 256, False), (16384, 8, 256, True)]
+
+
+@pytest.mark.parametrize("T,k,E,heavy", SORT_SIZES,
+                         ids=lambda v: str(v))
+def test_sort_chunk_sizes(T, k, E, heavy, dev):
+    hi = synth.uniform_codes(31, 7, (T, k), 0, 255).astype(np.int32)
+    lo = synth.uniform_codes(31, 8, (T, k), 0, 255).astype(np.int32)
+    ids = ((hi << 8) | lo) % E
+    if heavy:
+        ids.reshape(-1)[np.arange(T * k) % 4 != 0] = E // 3
+    log(f"sort T={T} k={k} E={E} heavy={heavy}")
+    want = oracle.sort(ids, E)
+    got = moe.sort_permute(torch.from_numpy(ids).to(dev), E)
+    torch.cuda.synchronize()
+    for g, w, what in zip(got, want, ("counts", "offsets", "sorted_pair", "pair_pos")):
+        assert np.array_equal(g.cpu().numpy(), w), what
+
+
 @pytest.mark.parametrize("shape", [synth.Shape(T=16, H=256, I=128, E=8, k=2, seed=0),
                                    synth.Shape(T=3, H=384, I=640, E=5, k=2, seed=7),
                                    synth.Shape(T=8, H=4096, I=1536, E=64, k=6, seed=1)])
