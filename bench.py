@@ -281,9 +281,11 @@ def cpu_baseline(name: str, budget_s: float):
         oracle.layer_tokens(inp, order[n_tok % T:n_tok % T + 1])
         n_tok += 1
     dt = time.perf_counter() - t0
+    drawn = (f"{n_tok} of the {T} tokens of the {name} workload (seeded random draw)" if n_tok <= T else
+             f"the {T} tokens of the {name} workload in seeded random order, cycled: {n_tok} token layers")
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
-            "sample": f"{n_tok} of the {T} tokens of the {name} workload (seeded random draw), whole layer "
-                      f"per token in {dt:.1f} s ({oracle.PRECISION} plain C, OpenMP over output rows)"}
+            "sample": f"{drawn}, whole layer per token in {dt:.1f} s ({oracle.PRECISION} plain C, "
+                      f"OpenMP over output rows)"}
 
 
 def cpu_baseline_dense(name: str, budget_s: float):
