@@ -274,12 +274,14 @@ size_t prefill_stage_bytes(long P, int E, int H, int I);
 hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
                              const uint8_t* xs, const int32_t* offsets,
                              const int32_t* sorted_pair, int T, int k, uint8_t* hq, uint8_t* hs,
-                             void* tile_ws, hipStream_t s);
-// tiles_ready: tile_ws already holds the token-tile list of these offsets
-// (launch_up_prefill built it there), so the down launch does not rebuild it.
+                             bool hs_by_step, void* tile_ws, hipStream_t s);
+// hs_by_step: hs [P, I/32] is written in the down GEMM's scale layout instead
+// (the dword of K-step j of row p at dword j P + p), for a chained down call.
+// chained: launch_up_prefill(hs_by_step) just ran on this tile_ws and these
+// offsets, so the token-tile list is there and hs is already by K-step.
 hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
                                const uint8_t* hs, const int32_t* offsets, int T, int k, uint16_t* O,
-                               void* tile_ws, bool tiles_ready, hipStream_t s);
+                               void* tile_ws, bool chained, hipStream_t s);
 hipError_t launch_combine(const uint16_t* O, const float* gates, const int32_t* pair_pos,
                           const uint16_t* O_shared, int T, int k, int H, float* y, hipStream_t s);
 // partial: router_ws_bytes(T, H, E) bytes of fp32 K-slice partial sums

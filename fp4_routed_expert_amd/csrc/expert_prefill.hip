@@ -339,6 +339,7 @@ struct KArgs {
   uint16_t* O;
   long P;
   int k, NF, H, I, QG, J;
+  int hs_by_step;             // gate/up: hs in the down GEMM's K-step layout (sT)
 };
 
 // One work item of a workgroup: a token tile (expert e, sorted rows m0 ..
@@ -550,7 +551,12 @@ __device__ __forceinline__ void run_item(const Item& cur, const Item& nxt, int b
             f32x4_to_e4m3(h0[0] * mul, h0[1] * mul, h0[2] * mul, h0[3] * mul);
         *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(hrow + 16) =
             f32x4_to_e4m3(h1[0] * mul, h1[1] * mul, h1[2] * mul, h1[3] * mul);
-        if (g == 0) hs[(size_t)(cur.m0 + r) * (I / 32) + q] = (uint8_t)sc;
+        // [P, I/32] row-major, or by K-step of the down GEMM: the dword of
+        // K-step q/4 of row p at dword (q/4) P + p, byte q % 4
+        const size_t p = (size_t)(cur.m0 + r);
+        const size_t at = ka.hs_by_step ? ((size_t)(q >> 2) * (size_t)ka.P + p) * 4 + (q & 3)
+                                        : p * (I / 32) + q;
+        if (g == 0) hs[at] = (uint8_t)sc;
       }
     } else {
       // lane holds token rows 16 (wm + 2i) + 4g + v, v < 4, column lane%16 of
@@ -768,7 +774,7 @@ size_t prefill_stage_bytes(long P, int E, int H, int I) {
 hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* xq,
                              const uint8_t* xs, const int32_t* offsets,
                              const int32_t* sorted_pair, int T, int k, uint8_t* hq, uint8_t* hs,
-                             void* tile_ws, hipStream_t s) {
+                             bool hs_by_step, void* tile_ws, hipStream_t s) {
   const long P = (long)T * k;
   int* hdr = static_cast<int*>(tile_ws);
   uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
@@ -794,20 +800,24 @@ hipError_t launch_up_prefill(const uint8_t* packed, const PackedLayout& L, const
   a.I = L.I;
   a.QG = L.I / 32;
   a.J = L.J;
+  a.hs_by_step = hs_by_step ? 1 : 0;
   hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(persistent_grid()), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, const uint8_t* hq,
                                const uint8_t* hs, const int32_t* offsets, int T, int k, uint16_t* O,
-                               void* tile_ws, bool tiles_ready, hipStream_t s) {
+                               void* tile_ws, bool chained, hipStream_t s) {
   const long P = (long)T * k;
   int* hdr = static_cast<int*>(tile_ws);
   uint32_t* sT = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(tile_ws) + tile_list_bytes(P, L.E));
-  hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64 + (tiles_ready ? 0 : 1))),
-                     dim3(64), 0, s, reinterpret_cast<const uint32_t*>(hs), L.J2,
-                     L.J2 % 4 == 0 && (uintptr_t)hs % 16 == 0, (const int32_t*)nullptr, k, P, sT,
-                     offsets, L.E, tiles_ready ? nullptr : hdr);
+  if (chained)  // the gate/up launch built the tile list and wrote hs by K-step
+    sT = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(hs));
+  else
+    hipLaunchKernelGGL(scales_by_step_kernel, dim3((unsigned)((P + 63) / 64 + 1)), dim3(64), 0, s,
+                       reinterpret_cast<const uint32_t*>(hs), L.J2,
+                       L.J2 % 4 == 0 && (uintptr_t)hs % 16 == 0, (const int32_t*)nullptr, k, P, sT,
+                       offsets, L.E, hdr);
   const int NF = (L.H + 255) / 256;
   KArgs a;
   a.wbase = packed + L.dnw_off;
@@ -827,6 +837,7 @@ hipError_t launch_down_prefill(const uint8_t* packed, const PackedLayout& L, con
   a.I = L.I;
   a.QG = L.H / 32;
   a.J = L.J2;
+  a.hs_by_step = 0;
   hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(persistent_grid()), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -274,10 +274,15 @@ size_t moe_fp4_stage_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, 
   return stage_ws_bytes(T, k, E, H, I);
 }
 
-moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, const uint8_t* xs,
-                               const int32_t* expert_offsets, const int32_t* sorted_pair,
-                               int32_t T, int32_t k, uint8_t* hq, uint8_t* hs, void* workspace,
-                               size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+}  // extern "C"
+
+// The gate/up stage; hs_by_step: on the prefill path, hs is written in the
+// down GEMM's scale layout for a chained expert_down call of the same chain.
+static moe_status_t expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, const uint8_t* xs,
+                              const int32_t* expert_offsets, const int32_t* sorted_pair, int32_t T,
+                              int32_t k, uint8_t* hq, uint8_t* hs, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, bool hs_by_step,
+                              hipStream_t stream) {
   moe_status_t st = check_weights(w);
   if (st != MOE_OK) return st;
   st = check_tek(T, w->E, k);
@@ -296,19 +301,30 @@ moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, co
   if (path == 1 && (int64_t)T * w->H >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   if (path == 1)
     return hip_status(launch_up_prefill(pk, L, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs,
-                                        workspace, stream));
+                                        hs_by_step, workspace, stream));
   return hip_status(launch_up_decode(pk, L, xq, xs, expert_offsets, sorted_pair, k, hq, hs,
                                      decode_row_groups((int64_t)T * k, w->E), stream));
 }
 
+extern "C" {
+
+moe_status_t moe_fp4_expert_up(const moe_fp4_weights_t* w, const uint8_t* xq, const uint8_t* xs,
+                               const int32_t* expert_offsets, const int32_t* sorted_pair,
+                               int32_t T, int32_t k, uint8_t* hq, uint8_t* hs, void* workspace,
+                               size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+  return expert_up(w, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs, workspace,
+                   workspace_bytes, flags, false, stream);
+}
+
 }  // extern "C"
 
-// The down stage; tiles_ready: the gate/up stage of the same call just ran
-// with this workspace and these offsets, so its token-tile list is reused.
+// The down stage; chained: expert_up(hs_by_step) of the same chain just ran
+// with this workspace and these offsets, so its token-tile list is reused and
+// hs is already in the down GEMM's scale layout.
 static moe_status_t expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, const uint8_t* hs,
                                 const int32_t* expert_offsets, int32_t T, int32_t k, uint16_t* O,
                                 void* workspace, size_t workspace_bytes, uint32_t flags,
-                                bool tiles_ready, hipStream_t stream) {
+                                bool chained, hipStream_t stream) {
   moe_status_t st = check_weights(w);
   if (st != MOE_OK) return st;
   st = check_tek(T, w->E, k);
@@ -324,7 +340,7 @@ static moe_status_t expert_down(const moe_fp4_weights_t* w, const uint8_t* hq, c
   const uint8_t* pk = static_cast<const uint8_t*>(w->packed);
   if (path == 1)
     return hip_status(launch_down_prefill(pk, L, hq, hs, expert_offsets, T, k, O, workspace,
-                                          tiles_ready, stream));
+                                          chained, stream));
   return hip_status(launch_down_decode(pk, L, hq, hs, expert_offsets, O,
                                        decode_row_groups((int64_t)T * k, w->E), stream));
 }
@@ -380,8 +396,8 @@ moe_status_t moe_fp4_grouped_forward(const moe_fp4_weights_t* w, const uint8_t* 
   uint16_t* O = reinterpret_cast<uint16_t*>(ws + c.O);
   void* stage = ws + c.stage;
   const size_t stage_bytes = c.total - c.stage;
-  st = moe_fp4_expert_up(w, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs, stage,
-                         stage_bytes, flags, stream);
+  st = expert_up(w, xq, xs, expert_offsets, sorted_pair, T, k, hq, hs, stage, stage_bytes, flags,
+                 true, stream);
   if (st != MOE_OK) return st;
   st = expert_down(w, hq, hs, expert_offsets, T, k, O, stage, stage_bytes, flags, true, stream);
   if (st != MOE_OK) return st;
@@ -544,8 +560,8 @@ moe_status_t moe_fp4_shared_expert(const moe_fp4_weights_t* w, const uint8_t* xq
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + c.offsets);
   st = hip_status(launch_identity_route(T, sorted, offsets, stream));
   if (st != MOE_OK) return st;
-  st = moe_fp4_expert_up(w, xq, xs, offsets, sorted, T, 1, ws + c.hq, ws + c.hs, ws + c.stage,
-                         c.total - c.stage, flags, stream);
+  st = expert_up(w, xq, xs, offsets, sorted, T, 1, ws + c.hq, ws + c.hs, ws + c.stage,
+                 c.total - c.stage, flags, true, stream);
   if (st != MOE_OK) return st;
   return expert_down(w, ws + c.hq, ws + c.hs, offsets, T, 1, O_shared, ws + c.stage,
                      c.total - c.stage, flags, true, stream);
