@@ -22,8 +22,9 @@
 // token tiles); its 16 waves take the K-steps in turn (wave w: steps w, w + 16, ...),
 // so at any moment they read neighbouring 4 KiB blocks, each keeping two steps
 // in flight; partial sums meet in LDS in wave order.  Prefill: LDS-tiled
-// GEMM, 128 tokens x 128 rows per workgroup, 128 K per stage, two register
-// sets so that one stage loads while another multiplies.
+// GEMM, 128 tokens x 128 rows (4 waves) or 192 tokens x 256 rows (8 waves)
+// per workgroup, 128 K per stage, two register sets so that one stage loads
+// while another multiplies.
 #include <atomic>
 
 #include "common.h"
