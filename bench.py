@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DENSE_DECODE_KERNEL = "dense_decode_kernel<16, 2, 2, true, 1>"   # the instantiations the library launches
-DENSE_PREFILL_KERNEL = "dense_prefill_kernel<2, 4, 6, 2, 1>"  # (prefill: the 192 x 256 tile)
+DENSE_PREFILL_KERNEL = "dense_dma_kernel"  # (prefill at the d3 shape: the 256 x 256 LDS-DMA tiles)
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 (and FP8 x FP4 scaled MFMA at the FP8 issue rate)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense FP4 x FP4 (reported beside: the mixed FP8 x FP4 MFMA issues at the FP8 rate)
@@ -359,7 +359,7 @@ def bench_dense(args):
                 "alg_bytes_per_launch": b_alg, "avg_launch_us": k_ms * 1e3}
     else:
         ach = f_alg / (k_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": DENSE_PREFILL_KERNEL + " (LDS-tiled FP8 GEMM)", "achieved": ach,
+        roof = {"bound": "mfma", "kernel": DENSE_PREFILL_KERNEL + " (LDS-DMA FP8 GEMM, 256 x 256 tiles)", "achieved": ach,
                 "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_FP8_PEAK_TFLOPS,
                 "traffic": load_traffic(DENSE_PREFILL_KERNEL, wl),
                 "alg_flops_per_launch": f_alg, "avg_launch_us": k_ms * 1e3}

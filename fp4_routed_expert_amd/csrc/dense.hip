@@ -22,12 +22,16 @@
 // token tiles); its 16 waves take the K-steps in turn (wave w: steps w, w + 16, ...),
 // so at any moment they read neighbouring 4 KiB blocks, each keeping two steps
 // in flight; partial sums meet in LDS in wave order.  Prefill: LDS-tiled
-// GEMM, 128 tokens x 128 rows (4 waves) or 192 tokens x 256 rows (8 waves)
-// per workgroup, 128 K per stage, two register sets so that one stage loads
-// while another multiplies.
+// GEMMs, 128 K per stage.  From a few thousand tokens (even K-step counts):
+// 256 tokens x 256 rows per workgroup, one wave per SIMD, the operands moved
+// by LDS-DMA (dense_dma_kernel); below that, or with an odd K-step count,
+// 128 x 128 (4 waves) or 192 x 256 (8 waves) tiles staged through two
+// register sets so that one stage loads while another multiplies.  The launch
+// takes the geometry with the fewest rounds of workgroups weighted by each
+// one's measured round time.
 #include <atomic>
 
-#include "common.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
@@ -448,6 +452,269 @@ __global__ __launch_bounds__(64 * kWM * kWN * kSplit) void dense_prefill_kernel(
     }
 }
 
+// ------------------------------------------------- prefill, LDS-DMA ring
+// 256 tokens x 256 weight rows per workgroup, 4 waves (one per SIMD, up to
+// 512 registers each) in a 2 x 2 grid: wave (wm, wn) owns tokens 128 wm ..
+// +128 (8 sub-tiles of 16) and weight tiles 8 wn .. 8 wn + 7 (128 rows), 64
+// MFMAs per K-step on 256 fp32 accumulators (AGPRs).  Against the
+// register-staged kernels a wave's tile is 2.7x larger, so the LDS fragment
+// reads per flop drop by a third, and the operands of a K-step travel from
+// global memory to LDS by LDS-DMA (no staging registers).  Two stages of
+// 66 KiB: the activation rows (row r's 16-byte chunk c at physical chunk
+// c ^ (r & 7), as in the expert GEMMs), the 16 weight tiles in packed order,
+// the rows' scale dwords and the tiles' scale bytes.
+// A K-step runs in two phases of 8 MFMA rows: phase 0 multiplies A fragment
+// n with weight tiles 0-3, phase 1 fragment n with tiles 4-7, so only half of
+// the weight fragments are live at a time.  Phase 1 opens with the step's one
+// barrier (after two MFMAs, so the pipe stays busy across it): it publishes
+// stage j + 1 and frees stage j's slot, whose refill (18 LDS-DMA loads per
+// wave) is spread over the following rows, three loads per row -- with one
+// wave per SIMD, any instruction that is not an MFMA keeps the matrix pipe
+// idle unless an MFMA is in flight (issuing the loads at once after the
+// barrier measured 11 % slower).  The next step's fragments are read in
+// phase 1 as their registers free up, six or more rows before their use.
+namespace dd {
+constexpr int kBM = 256, kBN = 256;
+constexpr int kA = kBM * 128;           // activation rows of a K-step
+constexpr int kB = kBN * 128;           // 16 weight tiles of 2 KiB
+constexpr int kSA = kBM * 4;            // a scale dword per row
+constexpr int kSB = (kBN / 32) * 128;   // 8 weight-tile pairs x 128 scale bytes
+constexpr int kStage = kA + kB + kSA + kSB;
+constexpr int kLoads = 18;              // DMA loads per wave per stage
+static_assert(kStage % 16 == 0, "stage alignment");
+}  // namespace dd
+
+// A wave's share of one stage's DMA: activation row groups w + 4u (u < 8, 8
+// rows of 128 B each), weight pairs 2w, 2w + 1 (4 KiB each as four 1 KiB
+// loads), the scale dwords of rows 64w .. 64w + 63 and the scale bytes of
+// weight pairs 2w, 2w + 1.  Few registers: the activation offsets are formed
+// at issue from the lane's first row (rows past T read row T - 1), the weight
+// pairs' offsets live in scalar bases.
+struct DDma {
+  const uint8_t* b0;  // weight pair 2w (or the last pair), K-step 0
+  const uint8_t* b1;  // weight pair 2w + 1
+  int row;            // the lane's activation row in group w (tile-relative token + m0)
+  uint32_t ach;       // the lane's 16-byte chunk: logical chunk (l%8) ^ (l/8) -- physical l%8
+  uint32_t sa, sb;    // scale offsets
+};
+
+// Load k (< 18) of the wave's share of K-step j's stage: 0-7 activation row
+// groups, 8-15 weight quarters, 16 row scales, 17 weight scales.
+__device__ __forceinline__ void dd_issue1(const DDma& d, const uint8_t* xq, const uint8_t* xs,
+                                          const uint8_t* psc, int T, int K, int j, uint32_t S,
+                                          int wave, int lane, int k) {
+  if (k < 8) {
+    dma_x4(wave_ptr(xq + (size_t)j * 128), (uint32_t)min(d.row + 32 * k, T - 1) * (uint32_t)K + d.ach,
+           S + 1024u * (uint32_t)(wave + 4 * k));
+  } else if (k < 16) {
+    const int u = k - 8;
+    dma_x4(wave_ptr((u < 4 ? d.b0 : d.b1) + (size_t)j * DenseLayout::kTileStep + 1024 * (u & 3)),
+           16u * (uint32_t)lane,
+           S + (uint32_t)dd::kA + 4096u * (uint32_t)(2 * wave + (u >> 2)) + 1024u * (uint32_t)(u & 3));
+  } else if (k == 16) {
+    dma_x1(wave_ptr(xs + (size_t)j * 4), d.sa, S + (uint32_t)(dd::kA + dd::kB) + 256u * (uint32_t)wave);
+  } else {
+    dma_x1(wave_ptr(psc + (size_t)j * DenseLayout::kScaleStep), d.sb,
+           S + (uint32_t)(dd::kA + dd::kB + dd::kSA) + 256u * (uint32_t)wave);
+  }
+}
+
+__device__ __forceinline__ void dd_issue(const DDma& d, const uint8_t* xq, const uint8_t* xs,
+                                         const uint8_t* psc, int T, int K, int j,
+                                         uint32_t stage_lds, int wave, int lane) {
+  const uint32_t S = wave_u32(stage_lds);
+#pragma unroll
+  for (int k = 0; k < dd::kLoads; ++k) dd_issue1(d, xq, xs, psc, T, K, j, S, wave, lane, k);
+}
+
+struct DDB {  // four weight fragments of a wave and their scale bytes
+  v8i b[4];
+  int sb[4];
+};
+
+// Per-lane LDS addresses of one stage slot, each the base of reads at small
+// constant offsets (the DS offset field holds 16 bits; the slots reach past
+// 64 KiB).  Laundered through an empty asm so that the compiler keeps them
+// as bases instead of folding them into one address with large offsets.
+struct DDAddr {
+  uint32_t alo, ahi;  // A row 128 wm + lane % 16, chunks g and g + 4 (sub-tile i at +2048 i)
+  uint32_t sa;        // its scale byte g (sub-tile i at +64 i)
+  uint32_t b;         // weight tile 8 wn, this lane's 16 bytes (tile t at +2048 t, second KiB +1024)
+  uint32_t sb;        // its scale byte (tile t at +64 t)
+};
+
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// The accumulating MFMA with its C operand tied to an AGPR tuple: with 256
+// accumulators per wave the compiler, left to itself, gives part of the
+// MFMAs a fresh destination and copies the accumulator (four moves and a
+// hazard wait per MFMA).  The asm is volatile so that the MFMAs keep their
+// order with the barrier and the DMA issue; its A, B and scale operands are
+// read at issue, and every register here is overwritten only several MFMAs
+// after its last use (the loop below), so no wait states are needed inside
+// the loop; the epilogue waits before reading the accumulators (dd_drain).
+__device__ __forceinline__ void dd_mfma(v4f& c, const v8i& a, const v8i& b, int sa, int sb) {
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(c)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+__device__ __forceinline__ DDAddr dd_addr(uint32_t slot, int wm, int wn, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const int row = 128 * wm + r;
+  DDAddr a;
+  a.alo = opaque(slot + (uint32_t)dswz(row, g));
+  a.ahi = opaque(slot + (uint32_t)dswz(row, g + 4));
+  a.sa = opaque(slot + (uint32_t)(dd::kA + dd::kB + 4 * row + g));
+  a.b = opaque(slot + (uint32_t)(dd::kA + 16384 * wn + 16 * lane));
+  a.sb = opaque(slot + (uint32_t)(dd::kA + dd::kB + dd::kSA + 512 * wn + lane));
+  return a;
+}
+
+__device__ __forceinline__ v4u lds_v4(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) v4u*>((uintptr_t)addr);
+}
+__device__ __forceinline__ int lds_u8v(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint8_t*>((uintptr_t)addr);
+}
+
+// weight tiles 4h .. 4h + 3 of the wave
+__device__ __forceinline__ void dd_read_b(DDB& f, const DDAddr& a, int h) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f.b[t] = cat8(lds_v4(a.b + 2048 * (4 * h + t)), lds_v4(a.b + 2048 * (4 * h + t) + 1024));
+    f.sb[t] = lds_u8v(a.sb + 64 * (4 * h + t));
+  }
+}
+
+__device__ __forceinline__ void dd_read_a(v8i& av, int& sa, const DDAddr& a, int i) {
+  av = cat8(lds_v4(a.alo + 2048 * i), lds_v4(a.ahi + 2048 * i));
+  sa = lds_u8v(a.sa + 64 * i);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dense_dma_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ xq,
+    const uint8_t* __restrict__ xs, int T, int N, int K, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * dd::kStage];
+  const DenseLayout L(N, K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int NTn = (N + dd::kBN - 1) / dd::kBN, NTm = (T + dd::kBM - 1) / dd::kBM;
+  int bm, bn;
+  if (!dense_tile_of(NTm, NTn, (int)blockIdx.x, bm, bn)) return;  // uniform: before any barrier
+  const int m0 = bm * dd::kBM, g0 = bn * (dd::kBN / 32);  // first token, first 32-row weight pair
+  const int ngroups = N / 32, J = L.J;
+
+  DDma d;
+  d.row = m0 + 8 * wave + (lane >> 3);
+  d.ach = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+  // weight pairs past N read the last pair (their columns are never stored)
+  d.b0 = wave_ptr(packed + (size_t)min(g0 + 2 * wave, ngroups - 1) * J * DenseLayout::kTileStep);
+  d.b1 = wave_ptr(packed + (size_t)min(g0 + 2 * wave + 1, ngroups - 1) * J * DenseLayout::kTileStep);
+  d.sa = (uint32_t)min(m0 + 64 * wave + lane, T - 1) * (uint32_t)(K / 32);
+  {
+    const int gg = min(g0 + 2 * wave + (lane >> 5), ngroups - 1);
+    d.sb = (uint32_t)((size_t)gg * J * DenseLayout::kScaleStep) + 4u * (uint32_t)(lane & 31);
+  }
+  const uint8_t* psc = packed + L.s_off;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds;
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  dd_issue(d, xq, xs, psc, T, K, 0, lds0, wave, lane);
+  dd_issue(d, xq, xs, psc, T, K, 1, lds0 + dd::kStage, wave, lane);
+  wait_vmcnt<dd::kLoads>();
+  __syncthreads();
+  const DDAddr ad0 = dd_addr(lds0, wm, wn, lane), ad1 = dd_addr(lds0 + dd::kStage, wm, wn, lane);
+  // Registers: the step's 8 A fragments, blo = weight tiles 0-3, bhi = tiles
+  // 4-7.  Phase 0 (rows n = 0..7) multiplies fragment n with tiles 0-3,
+  // phase 1 (n = 8..15) fragment n - 8 with tiles 4-7.  bhi is read at the
+  // second row; after it nothing reads stage j but fragments 6 and 7 (read at
+  // the first two rows), so phase 1 opens with the step's barrier and the
+  // refill of stage j's slot, then reads the next step's tiles 0-3 (blo is
+  // free) and its fragments one by one, each a row after its register's last
+  // use (fragment f at row 10 + f; 6 and 7 at the next step's rows 0 and 1),
+  // so every fragment is read six or more rows of MFMAs before it is used.
+  DDB blo, bhi;
+  v8i af[8];
+  int sf[8];
+  dd_read_b(blo, ad0, 0);
+#pragma unroll
+  for (int f = 0; f < 6; ++f) dd_read_a(af[f], sf[f], ad0, f);
+
+  auto step = [&](int j) {
+    const DDAddr& S = (j & 1) ? ad1 : ad0;
+    const DDAddr& Sn = (j & 1) ? ad0 : ad1;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int ph = n >> 3, i = n & 7;
+      if (n < 2) dd_read_a(af[6 + n], sf[6 + n], S, 6 + n);
+      if (n == 1) dd_read_b(bhi, S, 1);
+      if (n == 8) wait_vmcnt<0>();  // stage j + 1, the last one issued
+      if (n >= 10) dd_read_a(af[n - 10], sf[n - 10], Sn, n - 10);
+      const DDB& bb = ph ? bhi : blo;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dd_mfma(acc[i][4 * ph + t], af[i], bb.b[t], sf[i], bb.sb[t]);
+        if (n == 8 && t == 1) {
+          // two MFMAs in the pipe across the barrier, which publishes stage
+          // j + 1 and frees stage j's slot; then the next step's tiles 0-3
+          // (past the last K-step the last stage is loaded again and read,
+          // never used: the step has no branch)
+          __syncthreads();
+          dd_read_b(blo, Sn, 0);
+        }
+        // the refill of stage j's slot: three of its 18 loads after the
+        // second MFMA of each of phase 1's first six rows
+        if (n >= 8 && n < 14 && t == 1) {
+          const int jn = min(j + 2, J - 1);
+          const uint32_t Sl = wave_u32(lds0 + (uint32_t)((j & 1) * dd::kStage));
+          const int k0 = 3 * (n - 8);
+#pragma unroll
+          for (int k = k0; k < k0 + 3; ++k) dd_issue1(d, xq, xs, psc, T, K, jn, Sl, wave, lane, k);
+        }
+      }
+    }
+  };
+  for (int j = 0; j < J; j += 2) {
+    step(j);
+    step(j + 1);
+  }
+  // the last MFMAs' results are read below: 48 wait states (more than any
+  // MFMA's read-after-write distance), then the DMA of the stage loaded
+  // past the last K-step
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) asm volatile("" : "+a"(acc[i][t]));
+
+  // lane holds tokens 4g + v of column r of each 16 x 16 block; a token row's
+  // 256 bytes of the wave go out in 8 consecutive stores (t inner)
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = 32 * g0 + 128 * wn;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = m0 + 128 * wm + 16 * i + 4 * g + v;
+      if (tok < T) {
+        uint16_t* yrow = y + (size_t)tok * N + n0 + r;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (n0 + 16 * t < N) yrow[16 * t] = f32_to_bf16(acc[i][t][v]);
+      }
+    }
+}
+
 // The two geometries: 128 x 128 (4 waves) and 192 x 256 (8 waves; 256 x 256 does
 // not fit 2 waves per SIMD without spills).  The large tile stages fewer bytes
 // per flop (11 % faster on 4604 tokens) but a workgroup of either runs its
@@ -533,15 +800,22 @@ hipError_t launch_dense_prefill(const uint8_t* packed, const uint8_t* xq, const 
                         ((N + 16 * DSmall::BT - 1) / (16 * DSmall::BT));
   const long wg_large = (long)((T + DLarge::BM - 1) / DLarge::BM) *
                         ((N + 16 * DLarge::BT - 1) / (16 * DLarge::BT));
+  const long wg_dma = (long)((T + dd::kBM - 1) / dd::kBM) * ((N + dd::kBN - 1) / dd::kBN);
   const long slots_small = (long)occ.small * occ.ncu, slots_large = (long)occ.large * occ.ncu;
   const long rounds_small = (wg_small + slots_small - 1) / slots_small;
   const long rounds_large = (wg_large + slots_large - 1) / slots_large;
-  if (116 * rounds_large < 100 * rounds_small) {
-    const long blocks = (long)((T + DLarge::BM - 1) / DLarge::BM) *
-                        ((N + 16 * DLarge::BT - 1) / (16 * DLarge::BT));
-    hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets, 1>), dim3((unsigned)dense_grid(blocks)),
-                       dim3(DLarge::NT), 0, s,
-                       packed, xq, xs, T, N, K, y);
+  const long rounds_dma = (wg_dma + occ.ncu - 1) / occ.ncu;  // one per CU (its LDS)
+  // Each geometry's time is its rounds of workgroups times its round time,
+  // measured at K 16384, N 7168 against a round of small tiles: 1.16 for the
+  // 192 x 256 tiles, 1.06 for the 256 x 256 LDS-DMA kernel (which needs an
+  // even K-step count).
+  const long t_small = 100 * rounds_small, t_large = 116 * rounds_large;
+  if ((K / 128) % 2 == 0 && 106 * rounds_dma < (t_small < t_large ? t_small : t_large)) {
+    hipLaunchKernelGGL(dense_dma_kernel, dim3((unsigned)dense_grid(wg_dma)), dim3(256), 0, s, packed, xq,
+                       xs, T, N, K, y);
+  } else if (t_large < t_small) {
+    hipLaunchKernelGGL((dense_prefill_kernel<kLWM, kLWN, kLSM, kLSets, 1>), dim3((unsigned)dense_grid(wg_large)),
+                       dim3(DLarge::NT), 0, s, packed, xq, xs, T, N, K, y);
   } else if (wg_small <= occ.ncu) {
     // fewer small tiles than CUs: each tile's K-steps split over two wave groups
     hipLaunchKernelGGL((dense_prefill_kernel<2, 2, 4, 2, 2>), dim3((unsigned)dense_grid(wg_small)),

@@ -1,10 +1,11 @@
 """GPU parity of the FP8 dense projection, through the C ABI.
 
-y (bf16) against the oracle's fp64 sums on the same MXFP8 rows, on both
-paths (weight streaming and the LDS-tiled GEMM, in both of its tile
-geometries, the larger one taken when the smaller would need more rounds of
-workgroups, and the smaller one's K range split over two wave groups when
-its tiles are fewer than the CUs): the tiny workload, ragged
+y (bf16) against the oracle's sums on the same MXFP8 rows, on both
+paths (weight streaming and the LDS-tiled GEMM, in each of its tile
+geometries: 128 x 128, 192 x 256, and 256 x 256 by LDS-DMA for even K-step
+counts, taken by the fewest rounds of workgroups weighted by their round
+times, and the smaller one's K range split over two wave groups when its
+tiles are fewer than the CUs): the tiny workload, ragged
 token counts, an odd K-step count (the tiled kernel's zero padding step),
 weight-row counts that leave a partial 128-row tile, the decode-shaped and
 prefill-shaped projections at full size (sampled tokens), plus the prepacked
@@ -102,6 +103,25 @@ def test_dense_large_tile_geometry(dev):
     assert torch.equal(y.view(torch.int16), y_auto.view(torch.int16))
     toks = np.unique(np.concatenate([sample_tokens(c.sh.T, 40, seed=5), np.arange(1290, 1300)])).astype(np.int32)
     check_y(y.float().cpu().numpy()[toks], c.ref(toks), "dense/large-geometry")
+
+
+@pytest.mark.parametrize("K", [256, 1024, 2304])
+def test_dense_lds_dma_geometry(K, dev):
+    """2100 tokens x 4064 rows: 9 x 16 tiles of 256 x 256 fit one round on 256
+    CUs, where the 128 x 128 tiles would need two, so the LDS-DMA kernel runs
+    (K-step counts 2, 8 and 18: one, four and nine pairs of steps) -- ragged in
+    tokens (2100 = 8 x 256 + 52) and rows (4064 = 15 x 256 + 224, the last
+    tile's top weight pair re-reading the last one); every token against the
+    oracle, and the same bits run to run."""
+    c = get_dense("d0", dev, T=2100, K=K, N=4064)
+    log(f"[dense] LDS-DMA geometry T2100 K{K} N4064")
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    y = moe.dense_forward(c.dw, xq, xs)
+    y2 = moe.dense_forward(c.dw, xq, xs, PRE)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    toks = np.arange(c.sh.T, dtype=np.int32)
+    check_y(y.float().cpu().numpy(), c.ref(toks), f"dense/lds-dma/K{K}")
 
 
 def test_dense_small_tile_unsplit(dev):
