@@ -728,7 +728,7 @@ def measure_layer(args, cfg: str, steps: int, warmup: int) -> dict:
         line["config"]["workload"] += f" + router GEMM + {ns} shared expert(s)"
         line["config"]["n_shared"] = ns
         r_kernel = ("router_dma_kernel" if T >= 128 and E >= 256 else
-                    "router_tiled_kernel" if T >= 128 else "router_partial_kernel")
+                    "router_tiled_kernel" if T >= 128 or (T > 16 and E >= 256) else "router_partial_kernel")
         r_tflops = 2.0 * T * H * E / (r_ms * 1e-3) / 1e12
         line["router"] = {"bound": "hbm", "kernel": f"{r_kernel} + slice sum (bf16 x . Wg, fp32 logits)",
                           "achieved": r_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

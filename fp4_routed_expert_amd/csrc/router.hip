@@ -440,6 +440,10 @@ constexpr int kTiledMinT = 128;
 bool router_dma(int T, int H, int E) {
   return T >= kTiledMinT && E >= kDN && (long)T * H * 2 < (1L << 32) && (long)E * H * 2 < (1L << 32);
 }
+// The 128 x 128 LDS-tiled kernel from kTiledMinT tokens, and from 17 tokens
+// when the experts fill two of its tiles or more (E >= 256: stand-alone it
+// measured faster than the per-wave split-K kernel at every T from 16).
+bool router_tiled(int T, int E) { return T >= kTiledMinT || (T > 16 && E >= 2 * kTB); }
 
 }  // namespace
 
@@ -458,7 +462,7 @@ int router_slices(int T, int H, int E) {
     const int smax = H / 64 / 4 > 1 ? H / 64 / 4 : 1;
     return (int)(want < smax ? want : smax);
   }
-  if (T >= kTiledMinT) {
+  if (router_tiled(T, E)) {
     const long tiles = (long)((T + kTB - 1) / kTB) * ((E + kTB - 1) / kTB);
     const long want = 256 / tiles > 1 ? 256 / tiles : 1;
     const int smax = H / kTK / 4 > 1 ? H / kTK / 4 : 1;
@@ -499,7 +503,7 @@ hipError_t launch_router_partials(const uint16_t* x, const uint16_t* wg, int T, 
                        H, E, S, S > 1 ? partial : logits);
     return hipGetLastError();
   }
-  if (T >= kTiledMinT) {
+  if (router_tiled(T, E)) {
     const long tiles = (long)((T + kTB - 1) / kTB) * ((E + kTB - 1) / kTB);
     hipLaunchKernelGGL(router_tiled_kernel, dim3((unsigned)(tiles * S)), dim3(256), 2 * kTStage, s,
                        x, wg, T, H, E, S, S > 1 ? partial : logits);
