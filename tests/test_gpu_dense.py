@@ -89,6 +89,23 @@ def test_dense_full_size(cfg, ntok, dev):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+def test_dense_prefill_full_size_every_token_against_streaming(dev):
+    """d3 (T4604 K16384 N7168, the 256 x 256 LDS-DMA kernel): every token of
+    the tiled GEMM against the weight-streaming kernel forced on the same rows
+    (an independent kernel, fp32 sums in another order), plus sampled tokens
+    of both against the oracle."""
+    c = get_dense("d3", dev)
+    log("[dense] d3 every token: LDS-DMA tiles against forced streaming")
+    xq, xs = moe.quant_act_mxfp8(c.x)
+    y = moe.dense_forward(c.dw, xq, xs)
+    y_dec = moe.dense_forward(c.dw, xq, xs, DEC)
+    torch.cuda.synchronize()
+    check_y(y.float().cpu().numpy(), y_dec.float().cpu().numpy(), "dense/d3/tiled-vs-streaming")
+    toks = np.unique(np.concatenate([sample_tokens(c.sh.T, 8, seed=17), np.arange(4600, 4604)])).astype(np.int32)
+    ref = c.ref(toks)
+    check_y(y_dec.float().cpu().numpy()[toks], ref, "dense/d3/streaming")
+
+
 def test_dense_large_tile_geometry(dev):
     """1300 tokens x 7136 rows: the 128 x 128 tiles would need two rounds of
     workgroups on 256 CUs and the 192 x 256 tiles one, so the larger geometry

@@ -62,14 +62,16 @@ ROUTER_SHAPES = [
     (33, 512, 200),      # ragged tokens and experts [4]
     (300, 512, 16),      # LDS-tiled GEMM from T = 128 on [2]
     (777, 1536, 200),    # tiled, ragged tokens and experts [6]
-    (64, 7168, 256),     # decode batch [56]
+    (64, 7168, 256),     # decode batch: the LDS-tiled GEMM from T = 17 when E >= 256 [28]
     (16, 7168, 256),     # decode, wide [16]
     (1000, 1024, 96),    # [4]
     (4096, 256, 1024),   # LDS-DMA GEMM (E >= 256), four expert tiles, no K split [1]
-    (20, 256, 1024),     # the largest expert count, medium T [2]
+    (20, 256, 1024),     # the largest expert count, medium T: tiled, 8 expert tiles [1]
     (300, 128, 1000),    # LDS-DMA, ragged experts, two 64-K stages, no split [1]
     (300, 512, 256),     # LDS-DMA, ragged tokens [2]
     (777, 1536, 300),    # LDS-DMA, ragged tokens and experts, two expert tiles [6]
+    (100, 7168, 256),    # tiled below T = 128 (E >= 256), ragged tokens [28]
+    (48, 4096, 512),     # tiled below T = 128, four expert tiles [16]
     (129, 128, 256),     # LDS-DMA, one valid row in the second token tile [1]
 ]
 
