@@ -3,9 +3,12 @@
 One step = the whole layer on one batch of synthetic inputs already resident
 in HBM, as one library call (moe_fp4_layer_forward: routing, sort/permute,
 MXFP8 of x, gate/up GEMM + SwiGLU, down GEMM, combine), on one stream.
-The default workload is the decode-shaped layer (T=8, H=4096, I=1536, E=64,
-top-6).  Several copies of the packed weights are cycled so that the 256 MB
-Infinity Cache cannot serve a step's weights from the previous step.
+The default workload is the largest one, the prefill layer with Zipf-skewed
+routing (T=16384, H=7168, I=2048, E=256, top-8); after it the same process
+times the pages' prompt-length prefill (T=4604, reported as prefill_leg) and
+the decode layer (T=8, H=4096, I=1536, E=64, top-6, reported as decode_leg).
+Copies of the packed weights are cycled where one step's weights would fit
+the 256 MB Infinity Cache, so that it cannot serve them from the step before.
 
 Prints ONE JSON line (rank 0).  The dominant kernel (the gate/up expert GEMM)
 is timed with HIP events on the stream it runs on, bracketing each of its
@@ -13,8 +16,8 @@ launches in K further steps of the same layer run stage by stage through the
 single-stage calls right after the timed steps (same inputs, same weight
 copies); its algorithmic bytes (decode) or flops (prefill) per launch give
 the roofline fraction against 8 TB/s or the dense FP8 MFMA peak.  The CPU baseline is the
-oracle (a plain fp64 C implementation) on the host's cores, on a bounded
-sample of the same workload.
+oracle (plain C, fp32 accumulation) on the host's cores, on a bounded sample
+of the same workload.
 
 With --full a step starts from x alone (moe_fp4_layer_forward_full): the router
 logits come from a bf16 GEMM and --n-shared shared experts, packed after the
@@ -478,6 +481,9 @@ def main():
     ap.add_argument("--decode-leg", default="c1",
                     help="layer workload timed after the main one in the same process and reported "
                          "as decode_leg (the metric's HBM-bound part); '' = none")
+    ap.add_argument("--prefill-leg", default="c3",
+                    help="layer workload timed after the main one and reported as prefill_leg (the "
+                         "metric's other MFMA-bound shape); runs only with a decode leg ('' = none)")
     ap.add_argument("--flags", type=int, default=0, help="1 = force decode path, 2 = force prefill path")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 = skip")
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0 = auto)")
@@ -526,6 +532,16 @@ def main():
         return
 
     line = measure_layer(args, args.config, args.steps, args.warmup)
+    if args.decode_leg and args.prefill_leg and args.config != args.prefill_leg and not args.shard:
+        # the metric's other prefill shape (T4604, the pages' prompt length),
+        # same process, after the main workload's memory is released
+        import torch
+        torch.cuda.empty_cache()
+        p = measure_layer(args, args.prefill_leg, args.steps, args.warmup)
+        line["prefill_leg"] = {
+            "workload": p["config"]["workload"], "value": p["value"], "unit": p["unit"],
+            "ms_per_step": p["ms_per_step"], "step_ms_p10_p50_p90": p["step_ms_p10_p50_p90"],
+            "layer_mfma_frac_fp8": p["layer_mfma_frac_fp8"], "roofline": p["roofline"]}
     if args.decode_leg and args.config != args.decode_leg and not args.shard:
         # the decode-shaped leg of the metric (achieved HBM TB/s), same process,
         # after the prefill-shaped workload's memory is released
