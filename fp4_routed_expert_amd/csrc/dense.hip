@@ -551,15 +551,17 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 // The accumulating MFMA with its C operand tied to an AGPR tuple: with 256
 // accumulators per wave the compiler, left to itself, gives part of the
 // MFMAs a fresh destination and copies the accumulator (four moves and a
-// hazard wait per MFMA).  The asm is volatile so that the MFMAs keep their
-// order with the barrier and the DMA issue; its A, B and scale operands are
-// read at issue, and every register here is overwritten only several MFMAs
-// after its last use (the loop below), so no wait states are needed inside
-// the loop; the epilogue waits before reading the accumulators (dd_drain).
+// hazard wait per MFMA).  The asm is volatile and ordered with memory, so
+// that the MFMAs keep their order with the barrier and the DMA issue and every
+// LDS read stays where the loop below puts it: its A, B and scale operands
+// are read at issue, and each register is overwritten only a row of MFMAs or
+// more after its last use, so no wait states are needed inside the loop; the
+// epilogue waits before reading the accumulators.
 __device__ __forceinline__ void dd_mfma(v4f& c, const v8i& a, const v8i& b, int sa, int sb) {
   asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                : "+a"(c)
-               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+               : "v"(a), "v"(b), "v"(sa), "v"(sb)
+               : "memory");
 }
 
 __device__ __forceinline__ DDAddr dd_addr(uint32_t slot, int wm, int wn, int lane) {
